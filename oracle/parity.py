@@ -1,0 +1,63 @@
+"""Per-element error of a device result against the oracle.
+
+err_ij = |D~_ij - D*_ij| / ( |alpha| * ||Ahat_i,:||_2 * ||Bhat_:,j||_2 + |beta| * |C_ij| )
+
+D* is the unrounded fp64 oracle value and Ahat/Bhat the decoded, scaled
+operands.  The normaliser bounds |D*_ij| (Cauchy-Schwarz), so the error is
+relative to the size the dot product could have, not to a possibly cancelled
+result.  Where the normaliser is 0 the device value must equal D* rounded to
+the output element.  Any NaN in the device result fails.
+
+Bars: fp32 inputs 1e-5, bf16 inputs 2e-2, e4m3 inputs 6e-2 (max over
+elements).  Tighter regression bars, which reflect that both sides consume
+the same operand bytes so only fp32 accumulation order and the final
+rounding differ:
+  * fp32 output   : err <= 1e-5
+  * bf16 output   : |D~ - D*| <= 2^-8 |D*| + 1e-5 * normaliser
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+
+BARS = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
+
+
+def normaliser(row_norms, col_norms, alpha: float, beta: float, C=None):
+    den = abs(alpha) * np.outer(row_norms, col_norms)
+    if beta != 0.0 and C is not None:
+        den = den + abs(beta) * np.abs(C)
+    return den
+
+
+def normalised_error(D_dev, D_star, row_norms, col_norms, alpha: float, beta: float, C=None,
+                     out_elem: str = "f32"):
+    """Returns the per-element error array (inf where it fails outright)."""
+    D_dev = np.asarray(D_dev, dtype=np.float64)
+    den = normaliser(row_norms, col_norms, alpha, beta, C)
+    diff = np.abs(D_dev - D_star)
+    err = np.zeros_like(diff)
+    pos = den > 0
+    err[pos] = diff[pos] / den[pos]
+    zero = ~pos
+    if zero.any():
+        exact = codecs.round_to(D_star[zero], out_elem)
+        err[zero] = np.where(D_dev[zero] == exact, 0.0, np.inf)
+    err[np.isnan(D_dev)] = np.inf
+    return err
+
+
+def check(D_dev, D_star, row_norms, col_norms, alpha, beta, C, in_elem: str, out_elem: str):
+    """(ok, max_err, tight_ok, detail) under the bar of the input element and the
+    tight output-rounding bar."""
+    err = normalised_error(D_dev, D_star, row_norms, col_norms, alpha, beta, C, out_elem)
+    mx = float(err.max()) if err.size else 0.0
+    ok = mx <= BARS[in_elem]
+    den = normaliser(row_norms, col_norms, alpha, beta, C)
+    diff = np.abs(np.asarray(D_dev, dtype=np.float64) - D_star)
+    if out_elem == "f32":
+        tight = bool(np.all(err <= 1e-5))
+    else:
+        tight = bool(np.all(diff <= 2.0 ** -8 * np.abs(D_star) + 1e-5 * den))
+    return ok, mx, tight, {"max_err": mx, "n": int(err.size)}
