@@ -1,0 +1,210 @@
+"""ctypes binding of libdistgemm.so: argument marshalling only.
+
+Every name mirrors a C entry point of include/distgemm.h.  Device buffers may
+be passed as integers (device addresses) or as torch tensors, whose
+data_ptr() is passed; torch is used for nothing else.  There is no fallback:
+if the shared library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdistgemm.so")
+
+SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_C": 3,
+             "MONOLITHIC": 4}
+DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4}
+OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2}
+# bytes per element of (A/B, C/D) for each dtype
+ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
+              "E4M3_F32": (1, 4)}
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM", -5: "HIP"}
+
+# C functions declared in include/distgemm.h (checked by the CPU tests)
+C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
+               "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
+               "dist_gemm_step_times", "dist_gemm_destroy", "dist_gemm_last_error",
+               "dist_gemm_status_string")
+
+
+class DistGemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Step(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("shard", ctypes.c_int32), ("staged", ctypes.c_int32),
+                ("slot", ctypes.c_int32), ("m0", ctypes.c_int64), ("m1", ctypes.c_int64),
+                ("n0", ctypes.c_int64), ("n1", ctypes.c_int64)]
+
+    def as_tuple(self):
+        return (self.step, self.shard, bool(self.staged), self.slot, self.m0, self.m1, self.n0,
+                self.n1)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m communication_tensor_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.dist_gemm_step_table.argtypes = [i64, i64, i64, i64, i32, i32, i32,
+                                         ctypes.POINTER(Step), ctypes.POINTER(i32)]
+    lib.dist_gemm_plan.argtypes = [i64, i64, i64, i64, i32, i32, i32, ctypes.POINTER(vp)]
+    lib.dist_gemm_set_scales.argtypes = [vp, ctypes.c_float, ctypes.c_float]
+    lib.dist_gemm_set_option.argtypes = [vp, i32, i64]
+    lib.dist_gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+    lib.dist_gemm_plan_steps.argtypes = [vp, ctypes.POINTER(Step), ctypes.POINTER(i32)]
+    lib.dist_gemm_step_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.dist_gemm_destroy.argtypes = [vp]
+    lib.dist_gemm_last_error.argtypes = [vp]
+    lib.dist_gemm_last_error.restype = ctypes.c_char_p
+    lib.dist_gemm_status_string.argtypes = [i32]
+    lib.dist_gemm_status_string.restype = ctypes.c_char_p
+    for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
+                 "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
+                 "dist_gemm_step_times", "dist_gemm_destroy"):
+        getattr(lib, name).restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int, plan=None):
+    if rc != 0:
+        msg = lib.dist_gemm_last_error(plan)
+        raise DistGemmError(rc, msg.decode() if msg else "")
+
+
+def _enum(table, v):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def dist_gemm_step_table(M, N, K, L, TP, schedule, dtype) -> List[tuple]:
+    n = ctypes.c_int(0)
+    _check(lib.dist_gemm_step_table(M, N, K, L, TP, _enum(SCHEDULES, schedule),
+                                    _enum(DTYPES, dtype), None, ctypes.byref(n)))
+    arr = (Step * n.value)()
+    _check(lib.dist_gemm_step_table(M, N, K, L, TP, _enum(SCHEDULES, schedule),
+                                    _enum(DTYPES, dtype), arr, ctypes.byref(n)))
+    return [s.as_tuple() for s in arr]
+
+
+def dist_gemm_plan(M, N, K, L, TP, schedule, dtype) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(lib.dist_gemm_plan(M, N, K, L, TP, _enum(SCHEDULES, schedule), _enum(DTYPES, dtype),
+                              ctypes.byref(h)))
+    return h
+
+
+def dist_gemm_set_scales(plan, scale_a: float, scale_b: float):
+    _check(lib.dist_gemm_set_scales(plan, scale_a, scale_b), plan)
+
+
+def dist_gemm_set_option(plan, option, value: int):
+    _check(lib.dist_gemm_set_option(plan, _enum(OPTIONS, option), int(value)), plan)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def dist_gemm_run(plan, A, B, C, D, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    _check(lib.dist_gemm_run(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), alpha, beta,
+                             _stream(stream)), plan)
+
+
+def dist_gemm_plan_steps(plan) -> List[tuple]:
+    n = ctypes.c_int(0)
+    _check(lib.dist_gemm_plan_steps(plan, None, ctypes.byref(n)), plan)
+    arr = (Step * n.value)()
+    _check(lib.dist_gemm_plan_steps(plan, arr, ctypes.byref(n)), plan)
+    return [s.as_tuple() for s in arr]
+
+
+def dist_gemm_step_times(plan) -> List[float]:
+    n = ctypes.c_int(1024)
+    buf = (ctypes.c_float * 1024)()
+    _check(lib.dist_gemm_step_times(plan, buf, ctypes.byref(n)), plan)
+    return [buf[i] for i in range(n.value)]
+
+
+def dist_gemm_destroy(plan):
+    _check(lib.dist_gemm_destroy(plan))
+
+
+class Plan:
+    """Owning wrapper of a plan handle.  run() checks that tensor arguments
+    are large enough and on a GPU before handing their addresses over."""
+
+    def __init__(self, M, N, K, L=1, TP=1, schedule="MONOLITHIC", dtype="BF16_F32"):
+        self.M, self.N, self.K, self.L, self.TP = M, N, K, L, TP
+        self.schedule, self.dtype = schedule, dtype
+        self.handle = dist_gemm_plan(M, N, K, L, TP, schedule, dtype)
+
+    def set_scales(self, scale_a, scale_b):
+        dist_gemm_set_scales(self.handle, scale_a, scale_b)
+
+    def set_option(self, option, value):
+        dist_gemm_set_option(self.handle, option, value)
+
+    def steps(self):
+        return dist_gemm_plan_steps(self.handle)
+
+    def step_times(self):
+        return dist_gemm_step_times(self.handle)
+
+    def _need(self, t, nbytes, name):
+        if t is None or isinstance(t, int):
+            return
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+    def run(self, A, B, C, D, alpha=1.0, beta=0.0, stream=None):
+        ei, eo = ELEM_BYTES[self.dtype]
+        M, N, K, L = self.M, self.N, self.K, self.L
+        self._need(A, L * M * K * ei, "A")
+        self._need(B, L * N * K * ei, "B")
+        self._need(D, L * M * N * eo, "D")
+        if C is not None:
+            self._need(C, L * M * N * eo, "C")
+        dist_gemm_run(self.handle, A, B, C, D, alpha, beta, stream)
+
+    def close(self):
+        if self.handle is not None:
+            dist_gemm_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

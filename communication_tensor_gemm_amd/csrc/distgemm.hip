@@ -1,0 +1,509 @@
+// Host side of the TP-step GEMM library: validation, the step table, the
+// plan (staging slots, streams, events), the side-stream shard-copy engine
+// and the C ABI declared in include/distgemm.h.
+//
+// Mechanism (Distributed GEMM pull-request page, description): the operand
+// that arrives from a peer at every step is moved by the copy engine, not by
+// compute units, and each step's GEMM starts only after its operand is in
+// place.  On one GPU the peer's shard is a region of the caller's operand;
+// the copy engine here is SDMA (hipMemcpyDeviceToDeviceNoCU) on a side
+// stream, one copy per staged step, each followed by an event that the
+// step's GEMM launch waits on.  Step GEMMs alternate between the caller's
+// stream and a second compute stream by step parity (the stream alternation
+// of the PyTorch symmetric-memory page's all-gather consumer), so the last,
+// partly filled wave of one step's workgroups can overlap the next step.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/distgemm.h"
+#include "gemm_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+struct Problem {
+  int64_t M = 0, N = 0, K = 0, L = 0;
+  int S = 1;  // number of steps
+  int schedule = 0, dtype = 0;
+  int in_kind = 0, out_kind = 0;
+  int es_in = 0, es_out = 0;
+};
+
+int fail(std::string* where, int code, const std::string& msg) {
+  (where ? *where : g_last_error) = std::string(dist_gemm_status_string(code)) + ": " + msg;
+  return code;
+}
+
+int dtype_kinds(int dtype, int* in_kind, int* out_kind) {
+  switch (dtype) {
+    case DIST_GEMM_F32: *in_kind = dg::IN_F32; *out_kind = dg::OUT_F32; return 0;
+    case DIST_GEMM_BF16_F32: *in_kind = dg::IN_BF16; *out_kind = dg::OUT_F32; return 0;
+    case DIST_GEMM_BF16_BF16: *in_kind = dg::IN_BF16; *out_kind = dg::OUT_BF16; return 0;
+    case DIST_GEMM_E4M3_BF16: *in_kind = dg::IN_E4M3; *out_kind = dg::OUT_BF16; return 0;
+    case DIST_GEMM_E4M3_F32: *in_kind = dg::IN_E4M3; *out_kind = dg::OUT_F32; return 0;
+    default: return -1;
+  }
+}
+
+bool rows_schedule(int schedule) {
+  return schedule == DIST_GEMM_AG_ROT_A || schedule == DIST_GEMM_RS_TILE_A_ROT_C;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+             Problem* pr, std::string* err) {
+  if (M < 1 || N < 1 || K < 1 || L < 1) return fail(err, DIST_GEMM_ERR_INVALID_ARG, "M, N, K, L must be >= 1");
+  if (TP < 1) return fail(err, DIST_GEMM_ERR_INVALID_ARG, "TP must be >= 1");
+  if (schedule < DIST_GEMM_AG_ROT_A || schedule > DIST_GEMM_MONOLITHIC)
+    return fail(err, DIST_GEMM_ERR_INVALID_ARG, "unknown schedule " + std::to_string(schedule));
+  Problem p;
+  if (dtype_kinds(dtype, &p.in_kind, &p.out_kind) != 0)
+    return fail(err, DIST_GEMM_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+  if (TP > 1024) return fail(err, DIST_GEMM_ERR_SHAPE, "TP must be <= 1024");
+  if (M > INT32_MAX || N > INT32_MAX) return fail(err, DIST_GEMM_ERR_SHAPE, "M and N must be < 2^31");
+  if (L > 65535) return fail(err, DIST_GEMM_ERR_SHAPE, "L must be <= 65535");
+  p.es_in = dg::in_elem_size(p.in_kind);
+  p.es_out = dg::out_elem_size(p.out_kind);
+  if ((K * p.es_in) % 16 != 0)
+    return fail(err, DIST_GEMM_ERR_SHAPE,
+                "K * element size must be a multiple of 16 bytes (K=" + std::to_string(K) + ")");
+  if (static_cast<double>(K) * p.es_in * dg::kBM >= 2147483648.0)
+    return fail(err, DIST_GEMM_ERR_SHAPE, "K too large: 256 rows of K must span < 2 GiB");
+  p.M = M; p.N = N; p.K = K; p.L = L;
+  p.schedule = schedule; p.dtype = dtype;
+  p.S = schedule == DIST_GEMM_MONOLITHIC ? 1 : TP;
+  if (schedule != DIST_GEMM_MONOLITHIC) {
+    const int64_t ext = rows_schedule(schedule) ? M : N;
+    if (ext % TP != 0)
+      return fail(err, DIST_GEMM_ERR_SHAPE,
+                  std::string(rows_schedule(schedule) ? "M" : "N") + "=" + std::to_string(ext) +
+                      " is not divisible by TP=" + std::to_string(TP));
+  }
+  *pr = p;
+  return DIST_GEMM_OK;
+}
+
+// Step s of rank 0: the all-gather schedules consume their own shard first
+// and then shard (s + rank) mod S; the reduce-scatter schedules produce
+// chunk (rank + s + 1) mod S so that the own chunk comes last.
+std::vector<dist_gemm_step> build_steps(const Problem& p) {
+  std::vector<dist_gemm_step> v;
+  if (p.schedule == DIST_GEMM_MONOLITHIC) {
+    v.push_back({0, 0, 0, -1, 0, p.M, 0, p.N});
+    return v;
+  }
+  const int S = p.S;
+  const bool ag = p.schedule == DIST_GEMM_AG_ROT_A || p.schedule == DIST_GEMM_AG_ROT_B;
+  const bool rows = rows_schedule(p.schedule);
+  const int64_t w = (rows ? p.M : p.N) / S;
+  for (int s = 0; s < S; ++s) {
+    const int j = ag ? (s % S) : ((s + 1) % S);
+    dist_gemm_step st{};
+    st.step = s;
+    st.shard = j;
+    st.staged = s > 0 ? 1 : 0;
+    st.slot = s > 0 ? s - 1 : -1;
+    if (rows) {
+      st.m0 = j * w; st.m1 = (j + 1) * w; st.n0 = 0; st.n1 = p.N;
+    } else {
+      st.m0 = 0; st.m1 = p.M; st.n0 = j * w; st.n1 = (j + 1) * w;
+    }
+    v.push_back(st);
+  }
+  return v;
+}
+
+// Geometry of one staged shard: a 2-D region (height rows of width bytes,
+// src_pitch apart) of the source operand, copied densely into a slot.
+struct CopyGeom {
+  size_t width = 0, height = 0, src_pitch = 0;
+  size_t slot_bytes() const { return width * height; }
+};
+
+CopyGeom copy_geom(const Problem& p) {
+  CopyGeom g;
+  const size_t S = static_cast<size_t>(p.S);
+  switch (p.schedule) {
+    case DIST_GEMM_AG_ROT_A:  // A row shard, per batch contiguous
+      g.width = static_cast<size_t>(p.M / S) * p.K * p.es_in;
+      g.height = p.L;
+      g.src_pitch = static_cast<size_t>(p.M) * p.K * p.es_in;
+      break;
+    case DIST_GEMM_AG_ROT_B:  // B column shard = rows of the N x K storage
+      g.width = static_cast<size_t>(p.N / S) * p.K * p.es_in;
+      g.height = p.L;
+      g.src_pitch = static_cast<size_t>(p.N) * p.K * p.es_in;
+      break;
+    case DIST_GEMM_RS_TILE_A_ROT_C:  // C row chunk
+      g.width = static_cast<size_t>(p.M / S) * p.N * p.es_out;
+      g.height = p.L;
+      g.src_pitch = static_cast<size_t>(p.M) * p.N * p.es_out;
+      break;
+    case DIST_GEMM_RS_TILE_B_ROT_C:  // C column chunk: one strip per row
+      g.width = static_cast<size_t>(p.N / S) * p.es_out;
+      g.height = static_cast<size_t>(p.L) * p.M;
+      g.src_pitch = static_cast<size_t>(p.N) * p.es_out;
+      break;
+    default:
+      break;
+  }
+  return g;
+}
+
+}  // namespace
+
+struct dist_gemm_plan_s {
+  Problem pr;
+  std::vector<dist_gemm_step> steps;
+  CopyGeom geom;
+  int device = 0;
+  uint8_t* staging = nullptr;
+  size_t slot_stride = 0;
+  hipStream_t side = nullptr;  // copy engine stream
+  hipStream_t cs2 = nullptr;   // second compute stream
+  hipEvent_t ev_start = nullptr, ev_side_done = nullptr, ev_cs2_done = nullptr, ev_done = nullptr;
+  std::vector<hipEvent_t> ev_copy;
+  std::vector<hipEvent_t> t_begin, t_end;  // per-step timing
+  float scale_a = 1.0f, scale_b = 1.0f;
+  int compute_streams = 2;
+  int copy_engine = 0;
+  int step_timing = 0;
+  bool timed_last_run = false;
+  bool has_prev = false;
+  hipStream_t prev_stream = nullptr;
+  std::string err = "no error";
+};
+
+namespace {
+
+int hip_fail(std::string* err, hipError_t e, const char* what) {
+  return fail(err, DIST_GEMM_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                          hipGetErrorString(e) + ")");
+}
+
+#define DG_HIP(plan_err, call)                                  \
+  do {                                                          \
+    hipError_t e_ = (call);                                     \
+    if (e_ != hipSuccess) return hip_fail(plan_err, e_, #call); \
+  } while (0)
+
+void release(dist_gemm_plan_s* p) {
+  if (!p) return;
+  if (p->side) (void)hipStreamSynchronize(p->side);
+  if (p->cs2) (void)hipStreamSynchronize(p->cs2);
+  if (p->ev_done) (void)hipEventSynchronize(p->ev_done);
+  for (hipEvent_t e : p->ev_copy) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->t_begin) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->t_end) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {p->ev_start, p->ev_side_done, p->ev_cs2_done, p->ev_done})
+    if (e) (void)hipEventDestroy(e);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  if (p->cs2) (void)hipStreamDestroy(p->cs2);
+  if (p->staging) (void)hipFree(p->staging);
+  delete p;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+    else prev = -1;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+int enqueue_copy(dist_gemm_plan_s* P, const void* src_base, int shard, int slot) {
+  const CopyGeom& g = P->geom;
+  const Problem& pr = P->pr;
+  const uint8_t* src = static_cast<const uint8_t*>(src_base);
+  switch (pr.schedule) {
+    case DIST_GEMM_AG_ROT_A:
+    case DIST_GEMM_AG_ROT_B:
+    case DIST_GEMM_RS_TILE_A_ROT_C:
+      src += static_cast<size_t>(shard) * g.width;
+      break;
+    case DIST_GEMM_RS_TILE_B_ROT_C:
+      src += static_cast<size_t>(shard) * g.width;  // column offset within each row
+      break;
+    default:
+      return DIST_GEMM_OK;
+  }
+  uint8_t* dst = P->staging + static_cast<size_t>(slot) * P->slot_stride;
+  const hipMemcpyKind kind =
+      P->copy_engine == 0 ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+  hipError_t e;
+  if (g.height == 1)
+    e = hipMemcpyAsync(dst, src, g.width, kind, P->side);
+  else
+    e = hipMemcpy2DAsync(dst, g.width, src, g.src_pitch, g.width, g.height, kind, P->side);
+  if (e != hipSuccess) return hip_fail(&P->err, e, "shard copy");
+  return DIST_GEMM_OK;
+}
+
+// GEMM parameters of one step.
+dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, const void* A,
+                           const void* B, const void* C, void* D, float alpha, float beta) {
+  const Problem& pr = P->pr;
+  const int64_t M = pr.M, N = pr.N, K = pr.K;
+  const int64_t S = pr.S;
+  const int ei = pr.es_in, eo = pr.es_out;
+  const uint8_t* a = static_cast<const uint8_t*>(A);
+  const uint8_t* b = static_cast<const uint8_t*>(B);
+  const uint8_t* c = static_cast<const uint8_t*>(C);
+  uint8_t* d = static_cast<uint8_t*>(D);
+  const uint8_t* slot =
+      st.staged ? P->staging + static_cast<size_t>(st.slot) * P->slot_stride : nullptr;
+
+  dg::GemmParams g{};
+  g.K = static_cast<int32_t>(K);
+  g.L = static_cast<int32_t>(pr.L);
+  g.alpha = alpha;
+  g.beta = beta;
+  g.M = static_cast<int32_t>(st.m1 - st.m0);
+  g.N = static_cast<int32_t>(st.n1 - st.n0);
+  // defaults: operands in place
+  g.A = a + (st.m0 * K) * ei;  g.lda = K; g.sA = M * K;
+  g.B = b + (st.n0 * K) * ei;  g.ldb = K; g.sB = N * K;
+  g.C = c ? c + (st.m0 * N + st.n0) * eo : nullptr; g.ldc = N; g.sC = M * N;
+  g.D = d + (st.m0 * N + st.n0) * eo; g.ldd = N; g.sD = M * N;
+  if (st.staged) {
+    switch (pr.schedule) {
+      case DIST_GEMM_AG_ROT_A: g.A = slot; g.sA = (M / S) * K; break;
+      case DIST_GEMM_AG_ROT_B: g.B = slot; g.sB = (N / S) * K; break;
+      case DIST_GEMM_RS_TILE_A_ROT_C: g.C = slot; g.ldc = N; g.sC = (M / S) * N; break;
+      case DIST_GEMM_RS_TILE_B_ROT_C: g.C = slot; g.ldc = N / S; g.sC = M * (N / S); break;
+      default: break;
+    }
+  }
+  if (beta == 0.0f) g.C = nullptr;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dist_gemm_status_string(int status) {
+  switch (status) {
+    case DIST_GEMM_OK: return "DIST_GEMM_OK";
+    case DIST_GEMM_ERR_INVALID_ARG: return "DIST_GEMM_ERR_INVALID_ARG";
+    case DIST_GEMM_ERR_SHAPE: return "DIST_GEMM_ERR_SHAPE";
+    case DIST_GEMM_ERR_UNSUPPORTED: return "DIST_GEMM_ERR_UNSUPPORTED";
+    case DIST_GEMM_ERR_OOM: return "DIST_GEMM_ERR_OOM";
+    case DIST_GEMM_ERR_HIP: return "DIST_GEMM_ERR_HIP";
+    default: return "DIST_GEMM_ERR_UNKNOWN";
+  }
+}
+
+const char* dist_gemm_last_error(dist_gemm_plan_t plan) {
+  return plan ? plan->err.c_str() : g_last_error.c_str();
+}
+
+int dist_gemm_step_table(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule,
+                         int dtype, dist_gemm_step* out, int* n_steps) {
+  if (!n_steps) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "n_steps is NULL");
+  Problem pr;
+  const int rc = validate(M, N, K, L, TP, schedule, dtype, &pr, nullptr);
+  if (rc != DIST_GEMM_OK) return rc;
+  const std::vector<dist_gemm_step> st = build_steps(pr);
+  const int cap = *n_steps;
+  if (cap > 0 && !out) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "out is NULL");
+  for (int i = 0; i < cap && i < static_cast<int>(st.size()); ++i) out[i] = st[i];
+  *n_steps = static_cast<int>(st.size());
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+                   dist_gemm_plan_t* out) {
+  if (!out) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  Problem pr;
+  int rc = validate(M, N, K, L, TP, schedule, dtype, &pr, nullptr);
+  if (rc != DIST_GEMM_OK) return rc;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, DIST_GEMM_ERR_UNSUPPORTED,
+                std::string("this library is built for gfx950 only; device is ") + prop.gcnArchName);
+
+  auto* P = new dist_gemm_plan_s();
+  P->pr = pr;
+  P->device = dev;
+  P->steps = build_steps(pr);
+  P->geom = copy_geom(pr);
+  std::string* perr = nullptr;  // errors before the handle is returned go to the thread slot
+  const int n_slots = pr.S - 1;
+  if (pr.schedule != DIST_GEMM_MONOLITHIC && n_slots > 0) {
+    P->slot_stride = (P->geom.slot_bytes() + 255) & ~static_cast<size_t>(255);
+    e = hipMalloc(&P->staging, P->slot_stride * n_slots);
+    if (e != hipSuccess) {
+      release(P);
+      (void)hipGetLastError();
+      return fail(perr, DIST_GEMM_ERR_OOM, "staging allocation of " +
+                                               std::to_string(P->slot_stride * n_slots) + " bytes");
+    }
+  }
+  auto mk = [&](hipEvent_t* ev, unsigned flags) { return hipEventCreateWithFlags(ev, flags); };
+  e = hipStreamCreateWithFlags(&P->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&P->cs2, hipStreamNonBlocking);
+  if (e == hipSuccess) e = mk(&P->ev_start, hipEventDisableTiming);
+  if (e == hipSuccess) e = mk(&P->ev_side_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = mk(&P->ev_cs2_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = mk(&P->ev_done, hipEventDisableTiming);
+  P->ev_copy.assign(pr.S, nullptr);
+  P->t_begin.assign(pr.S, nullptr);
+  P->t_end.assign(pr.S, nullptr);
+  for (int s = 0; s < pr.S && e == hipSuccess; ++s) {
+    e = mk(&P->ev_copy[s], hipEventDisableTiming);
+    if (e == hipSuccess) e = mk(&P->t_begin[s], hipEventDefault);
+    if (e == hipSuccess) e = mk(&P->t_end[s], hipEventDefault);
+  }
+  if (e != hipSuccess) {
+    release(P);
+    return hip_fail(perr, e, "stream/event creation");
+  }
+  *out = P;
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b) {
+  if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
+  if (!std::isfinite(scale_a) || !std::isfinite(scale_b))
+    return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "scales must be finite");
+  plan->scale_a = scale_a;
+  plan->scale_b = scale_b;
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
+  if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
+  switch (option) {
+    case DIST_GEMM_OPT_COMPUTE_STREAMS:
+      if (value != 1 && value != 2)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "compute streams must be 1 or 2");
+      plan->compute_streams = static_cast<int>(value);
+      return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_COPY_ENGINE:
+      if (value != 0 && value != 1)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy engine must be 0 or 1");
+      plan->copy_engine = static_cast<int>(value);
+      return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_STEP_TIMING:
+      plan->step_timing = value ? 1 : 0;
+      return DIST_GEMM_OK;
+    default:
+      return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
+  }
+}
+
+int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
+                  float alpha, float beta, void* stream) {
+  if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
+  dist_gemm_plan_s* P = plan;
+  if (!A || !B || !D) return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "A, B and D must be non-NULL");
+  if (beta != 0.0f && !C) return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "C is NULL but beta != 0");
+  if (!std::isfinite(alpha) || !std::isfinite(beta))
+    return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "alpha and beta must be finite");
+  if (D == A || D == B) return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "D must not alias A or B");
+
+  DeviceGuard guard(P->device);
+  const Problem& pr = P->pr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool rotating = pr.schedule != DIST_GEMM_MONOLITHIC && pr.S > 1;
+  const bool two = P->compute_streams == 2 && pr.S > 1;
+  const float alpha_eff =
+      (pr.in_kind == dg::IN_E4M3) ? alpha * P->scale_a * P->scale_b : alpha;
+  const void* copy_src = nullptr;
+  switch (pr.schedule) {
+    case DIST_GEMM_AG_ROT_A: copy_src = A; break;
+    case DIST_GEMM_AG_ROT_B: copy_src = B; break;
+    default: copy_src = C; break;  // RS: the rotating partial
+  }
+  if (rotating && !copy_src) {
+    return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG,
+                "the reduce-scatter schedules rotate C: C must be non-NULL");
+  }
+
+  if (P->has_prev && P->prev_stream != st) DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_done, 0));
+  DG_HIP(&P->err, hipEventRecord(P->ev_start, st));
+  if (rotating) DG_HIP(&P->err, hipStreamWaitEvent(P->side, P->ev_start, 0));
+  if (two) DG_HIP(&P->err, hipStreamWaitEvent(P->cs2, P->ev_start, 0));
+
+  // Copy engine: every staged operand, in step order, one event per copy.
+  if (rotating) {
+    for (const dist_gemm_step& s : P->steps) {
+      if (!s.staged) continue;
+      int rc = enqueue_copy(P, copy_src, s.shard, s.slot);
+      if (rc != DIST_GEMM_OK) return rc;
+      DG_HIP(&P->err, hipEventRecord(P->ev_copy[s.step], P->side));
+    }
+  }
+  // Step GEMMs.
+  for (const dist_gemm_step& s : P->steps) {
+    hipStream_t cs = (two && (s.step & 1)) ? P->cs2 : st;
+    if (s.staged) DG_HIP(&P->err, hipStreamWaitEvent(cs, P->ev_copy[s.step], 0));
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_begin[s.step], cs));
+    const dg::GemmParams g = step_params(P, s, A, B, C, D, alpha_eff, beta);
+    DG_HIP(&P->err, dg::launch_gemm(pr.in_kind, pr.out_kind, g, cs));
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[s.step], cs));
+  }
+  // Join the side streams back into the caller's stream.
+  if (rotating) {
+    DG_HIP(&P->err, hipEventRecord(P->ev_side_done, P->side));
+    DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_side_done, 0));
+  }
+  if (two) {
+    DG_HIP(&P->err, hipEventRecord(P->ev_cs2_done, P->cs2));
+    DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_cs2_done, 0));
+  }
+  DG_HIP(&P->err, hipEventRecord(P->ev_done, st));
+  P->has_prev = true;
+  P->prev_stream = st;
+  P->timed_last_run = P->step_timing != 0;
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_steps) {
+  if (!plan || !n_steps) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan or n_steps is NULL");
+  const int cap = *n_steps;
+  if (cap > 0 && !out) return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "out is NULL");
+  for (int i = 0; i < cap && i < static_cast<int>(plan->steps.size()); ++i) out[i] = plan->steps[i];
+  *n_steps = static_cast<int>(plan->steps.size());
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n) {
+  if (!plan || !n) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan or n is NULL");
+  if (!plan->timed_last_run)
+    return fail(&plan->err, DIST_GEMM_ERR_UNSUPPORTED, "step timing was off for the last run");
+  DeviceGuard guard(plan->device);
+  const int S = static_cast<int>(plan->steps.size());
+  const int cap = *n;
+  if (cap > 0 && !ms) return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "ms is NULL");
+  DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+  for (int s = 0; s < S && s < cap; ++s)
+    DG_HIP(&plan->err, hipEventElapsedTime(&ms[s], plan->t_begin[s], plan->t_end[s]));
+  *n = S;
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_destroy(dist_gemm_plan_t plan) {
+  if (!plan) return DIST_GEMM_OK;
+  DeviceGuard guard(plan->device);
+  release(plan);
+  return DIST_GEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+/*
+ * distgemm.h -- C ABI of the MI355X (gfx950) TP-step GEMM library.
+ *
+ * The library computes, on one GPU, that GPU's share of a tensor-parallel
+ * GEMM
+ *
+ *     D = alpha * (scale_a * A) * (scale_b * B) + beta * C
+ *
+ * as the sequence of TP steps that one of the Distributed GEMM schedules
+ * prescribes (CUTLASS Distributed GEMM example page, "Trying out other
+ * schedules": AllGather1D_TilingCD_RotatingA / _RotatingB,
+ * ReduceScatter1D_TilingA_RotatingC / _TilingB_RotatingC; TP = number of
+ * GPUs = number of steps).  Per the Distributed GEMM pull-request page, the
+ * operand that would arrive from a peer at each step is moved by the copy
+ * engine while the GEMM of the previous step runs, and each step's GEMM
+ * waits for its operand before it starts.  On one GPU the peer's shard is a
+ * region of the caller's full operand; the library copies it device to
+ * device (SDMA, no compute units) into a plan-owned staging slot on a side
+ * stream, and the step GEMM reads it from there.
+ *
+ * Layouts (all row-major, element strides, batch index outermost):
+ *   A : L x M x K   (K contiguous, lda = K, batch stride M*K)
+ *   B : L x N x K   (the logical K x N operand stored K-contiguous,
+ *                    ldb = K, batch stride N*K)
+ *   C : L x M x N   (ldc = N, batch stride M*N)
+ *   D : L x M x N   (ldd = N, batch stride M*N)
+ * All pointers passed to dist_gemm_run are device pointers on the plan's
+ * device; the caller owns them.  Element types are fixed by the plan's
+ * dtype (see enum dist_gemm_dtype).
+ *
+ * Errors: every call returns DIST_GEMM_OK (0) or a negative code from enum
+ * dist_gemm_status.  A failed call leaves no work enqueued by that call
+ * except where noted, and records a message readable with
+ * dist_gemm_last_error(plan) (or dist_gemm_last_error(NULL) when there is
+ * no plan).  The library never exits or aborts the process.
+ */
+#ifndef DISTGEMM_H_
+#define DISTGEMM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dist_gemm_plan_s* dist_gemm_plan_t;
+
+enum dist_gemm_status {
+  DIST_GEMM_OK = 0,
+  DIST_GEMM_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, unknown enum */
+  DIST_GEMM_ERR_SHAPE = -2,       /* divisibility / alignment / size limit violated */
+  DIST_GEMM_ERR_UNSUPPORTED = -3, /* valid request this build cannot run */
+  DIST_GEMM_ERR_OOM = -4,         /* device allocation of plan resources failed */
+  DIST_GEMM_ERR_HIP = -5          /* a HIP runtime call failed (message holds hipError_t) */
+};
+
+/* Schedules.  Rank r = 0 (one GPU).  S = TP steps.
+ *   AG_ROT_A: step s consumes A row shard j = (r+s) mod S (rows
+ *     [j*M/S, (j+1)*M/S)) and writes those rows of D for all N columns.
+ *     Step 0 reads the local shard in place; steps 1..S-1 read a copy.
+ *   AG_ROT_B: step s consumes B column shard j = (r+s) mod S (rows
+ *     [j*N/S, (j+1)*N/S) of the N x K storage) and writes those columns of D.
+ *   RS_TILE_A_ROT_C: step s produces row chunk j = (r+s+1) mod S (own chunk
+ *     last): D[chunk] = alpha*A[chunk]*B + beta*C[chunk], where C[chunk] is
+ *     the rotating partial that arrives from the previous GPU; step 0 reads
+ *     it in place, steps 1..S-1 from a copy.  beta is normally 1.
+ *   RS_TILE_B_ROT_C: the same over column chunks of width N/S.
+ *   MONOLITHIC: one GEMM over the whole problem, no copies (the
+ *     single-device GEMM the pages' reference check compares against).
+ * The rotation orders are those of the PyTorch symmetric-memory page
+ * (_pipelined_all_gather_and_consume, _pipelined_produce_and_all2all). */
+enum dist_gemm_schedule {
+  DIST_GEMM_AG_ROT_A = 0,
+  DIST_GEMM_AG_ROT_B = 1,
+  DIST_GEMM_RS_TILE_A_ROT_C = 2,
+  DIST_GEMM_RS_TILE_B_ROT_C = 3,
+  DIST_GEMM_MONOLITHIC = 4
+};
+
+/* Element types (A/B in -> C/D out).  Accumulation is always fp32.
+ *   F32       : A,B fp32;            C,D fp32
+ *   BF16_F32  : A,B bf16;            C,D fp32
+ *   BF16_BF16 : A,B bf16;            C,D bf16 (round to nearest even)
+ *   E4M3_BF16 : A,B OCP e4m3fn;      C,D bf16; per-tensor scales apply
+ *   E4M3_F32  : A,B OCP e4m3fn;      C,D fp32; per-tensor scales apply
+ * The scaled fp8 form follows _scaled_mm's scale_a / scale_b on the PyTorch
+ * symmetric-memory page (fused_all_gather_scaled_matmul). */
+enum dist_gemm_dtype {
+  DIST_GEMM_F32 = 0,
+  DIST_GEMM_BF16_F32 = 1,
+  DIST_GEMM_BF16_BF16 = 2,
+  DIST_GEMM_E4M3_BF16 = 3,
+  DIST_GEMM_E4M3_F32 = 4
+};
+
+/* One row of the step table (host data). */
+typedef struct dist_gemm_step {
+  int32_t step;     /* s */
+  int32_t shard;    /* shard / chunk index j */
+  int32_t staged;   /* 1: operand arrives by a copy into a staging slot */
+  int32_t slot;     /* staging slot index (-1 when not staged) */
+  int64_t m0, m1;   /* row range of D written by this step */
+  int64_t n0, n1;   /* column range of D written by this step */
+} dist_gemm_step;
+
+/* Build the step table on the host, with no device work.  Validates exactly
+ * as dist_gemm_plan does.  Writes min(*n_steps on entry, TP) rows to `out`
+ * (which may be NULL when *n_steps is 0) and sets *n_steps to the number of
+ * steps.  Limits: 1 <= M, N <= 2^31-1; 1 <= L <= 65535; K >= 1 with
+ * K * element_size a multiple of 16 bytes; 256 * K * element_size < 2^31;
+ * 1 <= TP <= 1024; S | M (AG_ROT_A, RS_TILE_A_ROT_C) or S | N (AG_ROT_B,
+ * RS_TILE_B_ROT_C).  MONOLITHIC ignores TP for the step count (1 step). */
+int dist_gemm_step_table(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule,
+                         int dtype, dist_gemm_step* out, int* n_steps);
+
+/* Create a plan on the current HIP device: validates the problem (same
+ * rules as dist_gemm_step_table), builds the step table, allocates
+ * (TP-1) staging slots of one shard each (none for MONOLITHIC or TP = 1),
+ * one side stream for copies, one second compute stream, and the events
+ * that order them.  *out receives the handle (NULL on failure). */
+int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+                   dist_gemm_plan_t* out);
+
+/* Per-tensor dequantisation scales for the E4M3 dtypes (default 1.0 each).
+ * The epilogue multiplies the fp32 accumulator by alpha*scale_a*scale_b.
+ * Returns INVALID_ARG for a NULL plan or non-finite scales. */
+int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
+
+/* Tuning options (host state of the plan; take effect at the next run).
+ *   DIST_GEMM_OPT_COMPUTE_STREAMS: 1 = all step GEMMs on the caller's
+ *     stream; 2 (default) = steps alternate between the caller's stream and
+ *     the plan's second compute stream by step parity, so the tail of one
+ *     step's launch overlaps the next step (the alternation the PyTorch
+ *     symmetric-memory page uses for its all-gather consumer).
+ *   DIST_GEMM_OPT_COPY_ENGINE: 0 (default) = SDMA copy engine
+ *     (hipMemcpyDeviceToDeviceNoCU); 1 = the runtime's default device copy.
+ *   DIST_GEMM_OPT_STEP_TIMING: 1 = record a HIP event pair around every step
+ *     GEMM on the stream it is launched on; read with dist_gemm_step_times.
+ *     Default 0. */
+enum dist_gemm_option {
+  DIST_GEMM_OPT_COMPUTE_STREAMS = 0,
+  DIST_GEMM_OPT_COPY_ENGINE = 1,
+  DIST_GEMM_OPT_STEP_TIMING = 2
+};
+int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
+
+/* Enqueue the whole TP-step schedule on `stream` (a hipStream_t; NULL = the
+ * null stream) and return without waiting.  Completion of every step, copy
+ * and side-stream operation is ordered before any later work on `stream`.
+ *   A, B, D: required device pointers.  C: may be NULL iff beta == 0 (C is
+ *   not read when beta == 0).  D may alias C exactly (same pointer) for the
+ *   RS schedules and MONOLITHIC; no other overlap between D and A, B or C is
+ *   allowed.  A and B are only read.
+ * Buffers must stay allocated until the work completes on `stream`.  A run
+ * on another stream first waits for the plan's previous run.
+ * Errors: INVALID_ARG (NULL plan/A/B/D, C NULL with beta != 0, non-finite
+ * alpha/beta); HIP if an enqueue fails (earlier steps may be enqueued). */
+int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
+                  float alpha, float beta, void* stream);
+
+/* Query the plan's step table (same contents as dist_gemm_step_table). */
+int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_steps);
+
+/* With DIST_GEMM_OPT_STEP_TIMING set: wait for the last run to finish and
+ * write the per-step GEMM durations in milliseconds (min(*n, TP) values);
+ * *n receives the number of steps.  UNSUPPORTED if timing was off for the
+ * last run. */
+int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n);
+
+/* Synchronise the plan's streams, free its staging, streams and events, and
+ * the handle.  NULL is accepted (no-op). */
+int dist_gemm_destroy(dist_gemm_plan_t plan);
+
+/* Message of the last failure on `plan` (NULL: the last failure of a call
+ * without a plan, per thread).  Never NULL; valid until the next call. */
+const char* dist_gemm_last_error(dist_gemm_plan_t plan);
+
+/* Static name of a status code. */
+const char* dist_gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DISTGEMM_H_ */

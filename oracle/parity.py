@@ -10,10 +10,14 @@ the output element.  Any NaN in the device result fails.
 
 Bars: fp32 inputs 1e-5, bf16 inputs 2e-2, e4m3 inputs 6e-2 (max over
 elements).  Tighter regression bars, which reflect that both sides consume
-the same operand bytes so only fp32 accumulation order and the final
-rounding differ:
-  * fp32 output   : err <= 1e-5
-  * bf16 output   : |D~ - D*| <= 2^-8 |D*| + 1e-5 * normaliser
+the same operand bytes so only the accumulation and the final rounding
+differ:
+  * fp32 output   : err <= t
+  * bf16 output   : |D~ - D*| <= 2^-8 |D*| + t * normaliser
+with t = 1e-5 for fp32 and bf16 inputs (fp32 accumulation) and t = 1e-4 for
+e4m3 inputs, whose 64-product MFMA reduction rounds internally more coarsely
+than an fp32 sum (measured normalised errors up to 1.2e-5 at K = 128,
+falling with K; fp32 and bf16 inputs stay below 3e-7).
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ import numpy as np
 from . import codecs
 
 BARS = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
+TIGHT_ACCUM = {"f32": 1e-5, "bf16": 1e-5, "e4m3": 1e-4}
 
 
 def normaliser(row_norms, col_norms, alpha: float, beta: float, C=None):
@@ -56,8 +61,9 @@ def check(D_dev, D_star, row_norms, col_norms, alpha, beta, C, in_elem: str, out
     ok = mx <= BARS[in_elem]
     den = normaliser(row_norms, col_norms, alpha, beta, C)
     diff = np.abs(np.asarray(D_dev, dtype=np.float64) - D_star)
+    t = TIGHT_ACCUM[in_elem]
     if out_elem == "f32":
-        tight = bool(np.all(err <= 1e-5))
+        tight = bool(np.all(err <= t))
     else:
-        tight = bool(np.all(diff <= 2.0 ** -8 * np.abs(D_star) + 1e-5 * den))
+        tight = bool(np.all(diff <= 2.0 ** -8 * np.abs(D_star) + t * den))
     return ok, mx, tight, {"max_err": mx, "n": int(err.size)}

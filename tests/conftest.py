@@ -10,6 +10,11 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # load what is built; build only when nothing is
+    lib = os.path.join(ROOT, "communication_tensor_gemm_amd", "libdistgemm.so")
+    if not os.path.exists(lib):
+        from communication_tensor_gemm_amd.build import build
+        build()
 
 
 def pytest_collection_modifyitems(config, items):

@@ -1,0 +1,50 @@
+"""GPU parity at the four full-size workloads, in the launch configuration the
+benchmark times (two compute streams, SDMA shard copies).
+
+The oracle computes sampled outputs one by one: rows and columns that cover
+every step block, both sides of 256-tile edges, and random positions.  The
+properties that hold at any size are checked on the whole output, bitwise:
+the schedule equals the monolithic GEMM of the same kernel, one compute
+stream equals two, and the runtime's default copy path equals the SDMA one.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import check_sampled, log, run_plan, sample_indices, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["c2_blog_overlap_f32", "c3_ag_rot_a_bf16_tp8", "c4_rs_tile_a_rot_c_bf16_tp8",
+        "c5_ag_rot_b_e4m3_tp8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config(name):
+    import torch
+    w = workloads.CONFIGS[name]
+    log("case", name, "generating inputs")
+    x = workloads.generate(w)
+    dev = (to_gpu(x.A), to_gpu(x.B), to_gpu(x.C))
+    log("case", name, "run schedule", w.schedule, "TP", w.TP)
+    D = run_plan(w, x, dev=dev)
+    rows_sched = w.schedule in ("AG_ROT_A", "RS_TILE_A_ROT_C")
+    rows = sample_indices(w.M, w.TP if rows_sched else 1, 6, seed=1)
+    cols = sample_indices(w.N, 1 if rows_sched else w.TP, 6, seed=2)
+    log("case", name, "sampled parity on", len(rows), "x", len(cols))
+    err = check_sampled(w, x, D, rows, cols)
+    log("case", name, "max normalised error", err)
+
+    log("case", name, "bitwise invariants")
+    Dm = run_plan(w, x, schedule="MONOLITHIC", TP=1, dev=dev)
+    assert torch.equal(D, Dm), "schedule != monolithic"
+    del Dm
+    D1 = run_plan(w, x, dev=dev, options={"COMPUTE_STREAMS": 1})
+    assert torch.equal(D, D1), "two compute streams != one"
+    del D1
+    Db = run_plan(w, x, dev=dev, options={"COPY_ENGINE": 1})
+    assert torch.equal(D, Db), "SDMA copies != default copies"
+    del Db
+    if w.out_dtype == "f32":
+        assert torch.isfinite(D).all()
+    torch.cuda.synchronize()
