@@ -50,6 +50,12 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m communication_tensor_gemm_amd.build`")
+    # One HIP runtime per process: torch's ROCm build loads its own
+    # libamdhip64 (soname libamdhip64.so.7) through an unversioned dependency.
+    # Loading torch first makes this library's libamdhip64.so.7 dependency
+    # resolve to that same runtime; loading it first would bring in a second
+    # runtime alongside torch's, and one of the two then sees no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.dist_gemm_step_table.argtypes = [i64, i64, i64, i64, i32, i32, i32,
@@ -141,8 +147,9 @@ def dist_gemm_plan_steps(plan) -> List[tuple]:
 
 
 def dist_gemm_step_times(plan) -> List[float]:
-    n = ctypes.c_int(1024)
-    buf = (ctypes.c_float * 1024)()
+    n = ctypes.c_int(0)
+    _check(lib.dist_gemm_step_times(plan, None, ctypes.byref(n)), plan)
+    buf = (ctypes.c_float * max(n.value, 1))()
     _check(lib.dist_gemm_step_times(plan, buf, ctypes.byref(n)), plan)
     return [buf[i] for i in range(n.value)]
 

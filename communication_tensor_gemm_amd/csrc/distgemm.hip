@@ -16,6 +16,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -168,12 +169,14 @@ struct dist_gemm_plan_s {
   hipStream_t cs2 = nullptr;   // second compute stream
   hipEvent_t ev_start = nullptr, ev_side_done = nullptr, ev_cs2_done = nullptr, ev_done = nullptr;
   std::vector<hipEvent_t> ev_copy;
-  std::vector<hipEvent_t> t_begin, t_end;  // per-step timing
+  // Per-step timing ring: event pairs for the last `step_timing` runs,
+  // indexed [run % step_timing][step].
+  std::vector<hipEvent_t> t_begin, t_end;
   float scale_a = 1.0f, scale_b = 1.0f;
   int compute_streams = 2;
   int copy_engine = 0;
   int step_timing = 0;
-  bool timed_last_run = false;
+  int64_t timed_runs = 0;  // runs recorded since timing was (re)enabled
   bool has_prev = false;
   hipStream_t prev_stream = nullptr;
   std::string err = "no error";
@@ -363,13 +366,7 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
   if (e == hipSuccess) e = mk(&P->ev_cs2_done, hipEventDisableTiming);
   if (e == hipSuccess) e = mk(&P->ev_done, hipEventDisableTiming);
   P->ev_copy.assign(pr.S, nullptr);
-  P->t_begin.assign(pr.S, nullptr);
-  P->t_end.assign(pr.S, nullptr);
-  for (int s = 0; s < pr.S && e == hipSuccess; ++s) {
-    e = mk(&P->ev_copy[s], hipEventDisableTiming);
-    if (e == hipSuccess) e = mk(&P->t_begin[s], hipEventDefault);
-    if (e == hipSuccess) e = mk(&P->t_end[s], hipEventDefault);
-  }
+  for (int s = 0; s < pr.S && e == hipSuccess; ++s) e = mk(&P->ev_copy[s], hipEventDisableTiming);
   if (e != hipSuccess) {
     release(P);
     return hip_fail(perr, e, "stream/event creation");
@@ -400,9 +397,28 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy engine must be 0 or 1");
       plan->copy_engine = static_cast<int>(value);
       return DIST_GEMM_OK;
-    case DIST_GEMM_OPT_STEP_TIMING:
-      plan->step_timing = value ? 1 : 0;
+    case DIST_GEMM_OPT_STEP_TIMING: {
+      if (value < 0 || value > 4096)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "step timing keeps 0..4096 runs");
+      DeviceGuard guard(plan->device);
+      if (plan->ev_done && plan->has_prev) (void)hipEventSynchronize(plan->ev_done);
+      for (hipEvent_t ev : plan->t_begin) if (ev) (void)hipEventDestroy(ev);
+      for (hipEvent_t ev : plan->t_end) if (ev) (void)hipEventDestroy(ev);
+      plan->t_begin.clear();
+      plan->t_end.clear();
+      plan->step_timing = 0;
+      plan->timed_runs = 0;
+      const size_t n = static_cast<size_t>(value) * plan->steps.size();
+      plan->t_begin.assign(n, nullptr);
+      plan->t_end.assign(n, nullptr);
+      for (size_t i = 0; i < n; ++i) {
+        hipError_t e = hipEventCreate(&plan->t_begin[i]);
+        if (e == hipSuccess) e = hipEventCreate(&plan->t_end[i]);
+        if (e != hipSuccess) return hip_fail(&plan->err, e, "timing event creation");
+      }
+      plan->step_timing = static_cast<int>(value);
       return DIST_GEMM_OK;
+    }
     default:
       return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }
@@ -451,13 +467,15 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
     }
   }
   // Step GEMMs.
+  const size_t tbase =
+      P->step_timing ? static_cast<size_t>(P->timed_runs % P->step_timing) * P->steps.size() : 0;
   for (const dist_gemm_step& s : P->steps) {
     hipStream_t cs = (two && (s.step & 1)) ? P->cs2 : st;
     if (s.staged) DG_HIP(&P->err, hipStreamWaitEvent(cs, P->ev_copy[s.step], 0));
-    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_begin[s.step], cs));
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_begin[tbase + s.step], cs));
     const dg::GemmParams g = step_params(P, s, A, B, C, D, alpha_eff, beta);
     DG_HIP(&P->err, dg::launch_gemm(pr.in_kind, pr.out_kind, g, cs));
-    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[s.step], cs));
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[tbase + s.step], cs));
   }
   // Join the side streams back into the caller's stream.
   if (rotating) {
@@ -471,7 +489,7 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
   DG_HIP(&P->err, hipEventRecord(P->ev_done, st));
   P->has_prev = true;
   P->prev_stream = st;
-  P->timed_last_run = P->step_timing != 0;
+  if (P->step_timing) ++P->timed_runs;
   return DIST_GEMM_OK;
 }
 
@@ -486,16 +504,23 @@ int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_step
 
 int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n) {
   if (!plan || !n) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan or n is NULL");
-  if (!plan->timed_last_run)
-    return fail(&plan->err, DIST_GEMM_ERR_UNSUPPORTED, "step timing was off for the last run");
+  if (!plan->step_timing || plan->timed_runs == 0)
+    return fail(&plan->err, DIST_GEMM_ERR_UNSUPPORTED, "no timed run recorded");
   DeviceGuard guard(plan->device);
-  const int S = static_cast<int>(plan->steps.size());
-  const int cap = *n;
+  const int64_t S = static_cast<int64_t>(plan->steps.size());
+  const int64_t R = std::min<int64_t>(plan->timed_runs, plan->step_timing);
+  const int64_t cap = *n;
   if (cap > 0 && !ms) return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "ms is NULL");
   DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
-  for (int s = 0; s < S && s < cap; ++s)
-    DG_HIP(&plan->err, hipEventElapsedTime(&ms[s], plan->t_begin[s], plan->t_end[s]));
-  *n = S;
+  int64_t w = 0;
+  for (int64_t r = plan->timed_runs - R; r < plan->timed_runs; ++r) {
+    const size_t base = static_cast<size_t>(r % plan->step_timing) * S;
+    for (int64_t s = 0; s < S; ++s, ++w)
+      if (w < cap)
+        DG_HIP(&plan->err,
+               hipEventElapsedTime(&ms[w], plan->t_begin[base + s], plan->t_end[base + s]));
+  }
+  *n = static_cast<int>(R * S);
   return DIST_GEMM_OK;
 }
 

@@ -134,9 +134,10 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
  *     symmetric-memory page uses for its all-gather consumer).
  *   DIST_GEMM_OPT_COPY_ENGINE: 0 (default) = SDMA copy engine
  *     (hipMemcpyDeviceToDeviceNoCU); 1 = the runtime's default device copy.
- *   DIST_GEMM_OPT_STEP_TIMING: 1 = record a HIP event pair around every step
- *     GEMM on the stream it is launched on; read with dist_gemm_step_times.
- *     Default 0. */
+ *   DIST_GEMM_OPT_STEP_TIMING: V > 0 = record a HIP event pair around every
+ *     step GEMM on the stream it is launched on, keeping the pairs of the
+ *     last V runs (V <= 4096); read with dist_gemm_step_times.  0 (default)
+ *     = off.  Setting it waits for the plan's last run and clears the record. */
 enum dist_gemm_option {
   DIST_GEMM_OPT_COMPUTE_STREAMS = 0,
   DIST_GEMM_OPT_COPY_ENGINE = 1,
@@ -161,10 +162,10 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
 /* Query the plan's step table (same contents as dist_gemm_step_table). */
 int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_steps);
 
-/* With DIST_GEMM_OPT_STEP_TIMING set: wait for the last run to finish and
- * write the per-step GEMM durations in milliseconds (min(*n, TP) values);
- * *n receives the number of steps.  UNSUPPORTED if timing was off for the
- * last run. */
+/* With DIST_GEMM_OPT_STEP_TIMING = V set: wait for the last run to finish and
+ * write the step GEMM durations in milliseconds of the last R = min(runs, V)
+ * timed runs, oldest run first, steps in order (R * steps values, at most *n
+ * written); *n receives R * steps.  UNSUPPORTED if no timed run exists. */
 int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n);
 
 /* Synchronise the plan's streams, free its staging, streams and events, and

@@ -79,3 +79,14 @@ def test_null_handles_are_rejected_without_gpu():
     n = ctypes.c_int(0)
     assert dg.lib.dist_gemm_step_table(8, 8, 16, 1, 2, 0, 0, None, None) == -1
     assert dg.lib.dist_gemm_plan_steps(None, None, ctypes.byref(n)) == -1
+
+
+def test_single_hip_runtime_in_process():
+    """The package must not bring a second libamdhip64 next to torch's."""
+    import subprocess
+    import sys
+    code = ("import communication_tensor_gemm_amd, torch;"
+            "m=open('/proc/self/maps').read();"
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert out.stdout.strip() == "1", out.stdout + out.stderr
