@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the TP-step GEMM on one MI355X.
+
+One "step" of this benchmark is one dist_gemm_run: the whole TP-step schedule
+(every shard copy and every step GEMM) over one set of resident synthetic
+operands.  The default workload is the AllGather1D_TilingCD_RotatingA share
+of one GPU at TP=8 of the <16384, 106496, 16384> GEMM that the Distributed
+GEMM pull-request page times (bf16 in, fp32 accumulate and out; per step
+2048 x 13312 x 16384).
+
+Printed: one JSON line on stdout.  Progress goes to stderr.
+  value        whole-run TFLOP/s = 2*M*N*K*L / (wall time per run)
+  roofline     the step GEMM kernel: algorithmic flops of one launch over
+               its mean duration, from HIP events recorded around every
+               launch on the stream it runs on, over the timed region
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + % MFMA peak of TP-step GEMM at TP=8 shard shapes, 1 MI355X"
+# MI355X dense MFMA peaks (TFLOP/s) by input element type
+PEAK = {"bf16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
+DEFAULT_CONFIG = "c3_ag_rot_a_bf16_tp8"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pick_config(name):
+    import workloads
+    if name in workloads.CONFIGS:
+        return workloads.CONFIGS[name]
+    hits = [k for k in workloads.CONFIGS if k.startswith(name)]
+    if len(hits) != 1:
+        raise SystemExit(f"unknown or ambiguous config {name!r}; choose from {list(workloads.CONFIGS)}")
+    return workloads.CONFIGS[hits[0]]
+
+
+def to_gpu(arr):
+    import numpy as np
+    import torch
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        arr = arr.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def timed_runs(plan, args_run, steps, warmup, timing_runs):
+    import torch
+    for _ in range(warmup):
+        plan.run(*args_run)
+    torch.cuda.synchronize()
+    if timing_runs:
+        plan.set_option("STEP_TIMING", steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.run(*args_run)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = plan.step_times() if timing_runs else []
+    return (t1 - t0) / steps * 1e3, step_ms
+
+
+def cpu_baseline(w, x, rows_per_block):
+    """The oracle (as it stands) on a sample: rows_per_block rows from each of
+    the S row blocks (or S x rows_per_block rows for column schedules), all N
+    columns, every step visited."""
+    import numpy as np
+    from oracle import gemm
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    S = w.TP if w.schedule != "MONOLITHIC" else 1
+    if w.schedule in ("AG_ROT_A", "RS_TILE_A_ROT_C"):
+        blk = w.M // S
+        rows = np.concatenate([np.arange(s * blk, s * blk + min(rows_per_block, blk))
+                               for s in range(S)])
+    else:
+        rows = np.arange(min(w.M, rows_per_block * S))
+    cols = np.arange(w.N)
+    t0 = time.perf_counter()
+    gemm.dist_gemm_sampled(x.A, x.B, x.C, w.alpha, w.beta, w.schedule, S, w.in_dtype,
+                           w.out_dtype, rows, cols, x.scale_a, x.scale_b)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * len(cols) * w.K
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or cores,
+            "host_cores": cores, "kind": "oracle", "seconds": dt,
+            "sample": f"{len(rows)} of {w.M} rows x all {w.N} columns x K={w.K} "
+                      f"({flops / 1e12:.3f} TFLOP), fp64 numpy matmul per step"}
+
+
+def parity_spot_check(w, x, D):
+    import numpy as np
+    import torch
+    from oracle import codecs, gemm, parity
+    g = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([g.integers(0, w.M, 48), [0, w.M - 1]]))
+    cols = np.unique(np.concatenate([g.integers(0, w.N, 48), [0, w.N - 1]]))
+    S = w.TP if w.schedule != "MONOLITHIC" else 1
+    Ds, rn, cn = gemm.dist_gemm_sampled(x.A, x.B, x.C, w.alpha, w.beta, w.schedule, S,
+                                        w.in_dtype, w.out_dtype, rows, cols, x.scale_a,
+                                        x.scale_b)
+    sub = D[0].index_select(0, torch.from_numpy(rows).cuda()).index_select(
+        1, torch.from_numpy(cols).cuda()).cpu().numpy()
+    got = sub.astype(np.float64) if w.out_dtype == "f32" else codecs.bf16_to_f64(sub.view(np.uint16))
+    c = None if w.beta == 0 else codecs.decode(x.C[0][np.ix_(rows, cols)], w.out_dtype)
+    ok, mx, tight, _ = parity.check(got, Ds, rn, cn, w.alpha, w.beta, c, w.in_dtype, w.out_dtype)
+    return {"ok": bool(ok and tight), "max_normalised_err": mx, "n": int(got.size)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--compute-streams", type=int, default=2)
+    ap.add_argument("--copy-engine", type=int, default=0, help="0 SDMA, 1 runtime default")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="oracle sample: rows per step block for the CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--no-mono", action="store_true", help="skip the monolithic comparison")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build "
+              "times one GPU's share of the TP schedule; multi-GPU runs are not part of it.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import communication_tensor_gemm_amd as dg
+    import workloads
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = pick_config(args.config)
+    S = w.TP if w.schedule != "MONOLITHIC" else 1
+    log(f"[bench] workload {w.name}: {w.schedule} {w.dtype} M={w.M} N={w.N} K={w.K} TP={w.TP}")
+    t = time.perf_counter()
+    x = workloads.generate(w)
+    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f}s")
+    A, B, C = to_gpu(x.A), to_gpu(x.B), to_gpu(x.C)
+    out_dt = torch.float32 if w.out_dtype == "f32" else torch.int16
+    D = torch.empty((w.L, w.M, w.N), dtype=out_dt, device="cuda")
+
+    plan = dg.Plan(w.M, w.N, w.K, w.L, w.TP, w.schedule, w.dtype)
+    if w.in_dtype == "e4m3":
+        plan.set_scales(x.scale_a, x.scale_b)
+    plan.set_option("COMPUTE_STREAMS", args.compute_streams)
+    plan.set_option("COPY_ENGINE", args.copy_engine)
+    run_args = (A, B, C if w.beta != 0 else None, D, w.alpha, w.beta)
+    log(f"[bench] timing {args.steps} runs after {args.warmup} warmup runs")
+    ms, step_ms = timed_runs(plan, run_args, args.steps, args.warmup, True)
+    value = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK[w.in_dtype]
+    launch_ms = float(np.mean(step_ms))
+    flops_per_launch = w.flops / S
+    achieved = flops_per_launch / (launch_ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/run, {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak); "
+        f"step GEMM {launch_ms:.3f} ms avg -> {achieved:.1f} TFLOP/s")
+
+    parity = parity_spot_check(w, x, D)
+    log(f"[bench] parity spot check: {parity}")
+
+    mono = None
+    if not args.no_mono:
+        with dg.Plan(w.M, w.N, w.K, w.L, 1, "MONOLITHIC", w.dtype) as mp:
+            if w.in_dtype == "e4m3":
+                mp.set_scales(x.scale_a, x.scale_b)
+            mono_ms, mono_steps = timed_runs(mp, run_args, args.steps, args.warmup, True)
+        mono = {"ms": mono_ms, "tflops": w.flops / (mono_ms * 1e-3) / 1e12,
+                "kernel_ms": float(np.mean(mono_steps)),
+                "exposed_overhead": ms / mono_ms - 1.0}
+        log(f"[bench] monolithic {mono_ms:.3f} ms ({mono['tflops']:.1f} TFLOP/s); "
+            f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
+    plan.close()
+    del A, B, C, D
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] CPU oracle baseline on a sample ({args.cpu_rows} rows per step block)")
+        cpu = cpu_baseline(w, x, args.cpu_rows)
+        log(f"[bench] CPU oracle {cpu['value'] * 1e3:.1f} GFLOP/s in {cpu['seconds']:.1f}s")
+
+    dtype_name = {"bf16": "bf16", "f32": "f32", "e4m3": "e4m3"}[w.in_dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "schedule": w.schedule, "M": w.M, "N": w.N, "K": w.K,
+                   "L": w.L, "TP": w.TP, "in": w.in_dtype, "out": w.out_dtype,
+                   "alpha": w.alpha, "beta": w.beta, "compute_streams": args.compute_streams,
+                   "copy_engine": "sdma" if args.copy_engine == 0 else "runtime_default"},
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "gemm_tn_kernel (one launch per TP step)",
+                     "launch_ms": round(launch_ms, 4), "launches_per_step": S},
+        "monolithic": mono,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
