@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed fp32 arithmetic stays off (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the heuristic otherwise puts them in arch
+    # VGPRs and spills the fragment buffers of the 4-stage pipeline
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
