@@ -125,6 +125,49 @@ def parity_spot_check(w, x, D):
     return {"ok": bool(ok and tight), "max_normalised_err": mx, "n": int(got.size)}
 
 
+KERNEL_SOURCES = ["communication_tensor_gemm_amd/csrc/gemm_tile.h",
+                  "communication_tensor_gemm_amd/csrc/gemm_mfma16.hip",
+                  "communication_tensor_gemm_amd/csrc/gemm_mfma_f8.hip"]
+TRAFFIC_FILE = "profiles/gemm_tn_kernel_hbm_traffic.txt"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per step-kernel launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_sources_sha256_16") != kernel_source_hash():
+        return None
+    v = rec.get(f"{workload}.bytes_per_launch")
+    return float(v) if v else None
+
+
+def calibrate_copy(nbytes, reps):
+    """A plain device-to-device copy of known size (the scale reference for
+    the HBM byte counters): reps copies of nbytes each."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,7 +180,13 @@ def main():
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-mono", action="store_true", help="skip the monolithic comparison")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run plain copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 3)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build "
@@ -223,7 +272,8 @@ def main():
                    "copy_engine": "sdma" if args.copy_engine == 0 else "runtime_default"},
         "pct_mfma_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(w.name),
                      "kernel": "gemm_tn_kernel (one launch per TP step)",
                      "launch_ms": round(launch_ms, 4), "launches_per_step": S},
         "monolithic": mono,

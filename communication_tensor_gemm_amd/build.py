@@ -15,7 +15,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdistgemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["gemm_kernels.hip", "distgemm.hip"]
+SOURCES = ["gemm_mfma16.hip", "gemm_mfma_f8.hip", "distgemm.hip"]
+# per-source extra flags
+EXTRA = {
+    # 16 x 16 MFMA family: accumulators in VGPR form, or the compiler spills
+    # the fragment buffers; the e4m3 family spills under that form instead
+    "gemm_mfma16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -26,9 +32,6 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed fp32 arithmetic stays off (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs: the heuristic otherwise puts them in arch
-    # VGPRs and spills the fragment buffers of the 4-stage pipeline
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
@@ -61,7 +64,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *HIPCC_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = OUT + ".tmp"

@@ -1,4 +1,4 @@
-// gfx950 (CDNA4) MFMA GEMM with an alpha/beta epilogue: the per-step GEMM of
+// gemm_tile.h -- gfx950 (CDNA4) MFMA GEMM with an alpha/beta epilogue: the per-step GEMM of
 // the TP schedules (the dense GEMM that the Distributed GEMM pull-request
 // page runs at every step, written here for MI355X).
 //
@@ -13,36 +13,38 @@
 //          neutral E8M0 block scales; per-tensor scales go to the epilogue)
 //
 // Data movement.  Both operands are K-contiguous ("TN"), so a lane's MFMA
-// fragment is 16 contiguous bytes of one row (ds_read_b128).  Slabs move
-// from global memory straight into LDS with buffer_load_dwordx4 ... lds:
-// each wave instruction fills 1 KiB of LDS (lane l -> bytes 16l..16l+15),
-// so the LDS layout is chosen by which global chunk each lane fetches.
-// Rows are 64 bytes; the four 16-byte chunks of row r are stored XOR-
-// permuted by f(r) = ((r>>1) ^ (r>>2)) & 3, which puts the 16 rows that 16
-// lanes read in one LDS cycle on distinct banks.  The buffer descriptor of
-// each operand covers only the tile's valid rows, so rows past M or N load
-// as zeros (out-of-range lanes of an LDS load write zeros), and slabs past K
-// are pushed out of range by setting the offset's top bit.
+// fragment is 16 contiguous bytes of one row (ds_read_b128).  K is walked in
+// slabs of 128 bytes per row (one cache line), moved from global memory
+// straight into LDS with buffer_load_dwordx4 ... lds: each wave instruction
+// fills 1 KiB of LDS (lane l -> bytes 16l..16l+15), eight whole rows, so the
+// L1 asks L2 for full 128-byte lines (64-byte requests halve the bytes per
+// outstanding request and measured about half the L2 -> LDS rate).  Within a
+// 64-byte half row the four 16-byte chunks of row r are stored XOR-permuted
+// by f(r) = ((r>>1) ^ (r>>2)) & 3, which puts the 16 rows that 16 lanes read
+// in one LDS cycle on distinct banks (zero bank conflicts measured).  The
+// buffer descriptor of each operand covers only the tile's valid rows, so
+// rows past M or N load as zeros (out-of-range lanes of an LDS load write
+// zeros), and chunks past K are pushed out of range by the offset's top bit.
 //
-// Pipeline.  Four LDS stages of 32 KiB (A and B slabs) form a ring.  Each
-// iteration: wait for this wave's fragment reads of slab k and its loads of
-// slab k+1, one barrier (every wave now holds slab k in registers, and slab
-// k+1 is complete in LDS), issue the loads of slab k+4 into the stage slab
-// k just vacated, issue the fragment reads of slab k+1, then run slab k's
-// MFMAs.  Loads therefore run four slabs (about 4000 MFMA cycles) ahead,
-// and fragment reads one slab ahead of the MFMAs that consume them.
+// Pipeline.  Two LDS stages of 64 KiB (A and B slabs).  MFMAs walk half
+// slabs; fragments of the next half slab are read while the current one is
+// multiplied.  At the end of each slab one barrier certifies that every
+// wave holds the slab in registers and that the next slab has landed; the
+// slab after next is then loaded into the stage just vacated, so loads run
+// one slab (about 2000 MFMA cycles) ahead.
 //
 // Workgroup -> tile mapping is XCD-aware: MI355X places workgroup b on XCD
 // b mod 8, so each XCD gets one contiguous range of the tile order, and
 // that order walks groups of 8 tile rows column by column, so the tiles an
 // XCD runs together share A rows and B columns in its own L2.
+#pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "gemm_launch.h"
 
 namespace dg {
-namespace {
+namespace tile {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -51,12 +53,12 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kThreads = 256;
-constexpr int kSlab = 64;                         // bytes of K per operand row per stage
-constexpr int kOperandStage = kBM * kSlab;        // 16 KiB
-constexpr int kStageBytes = 2 * kOperandStage;    // A + B = 32 KiB
-constexpr int kStages = 4;
-constexpr int kLoadsPerOperand = kOperandStage / 1024 / 4;  // per wave: 4
-constexpr int kLoadsPerSlab = 2 * kLoadsPerOperand;         // per wave: 8
+constexpr int kSlab = 128;                        // bytes of K per operand row per stage
+constexpr int kHalf = 64;                         // fragment reads walk half slabs
+constexpr int kOperandStage = kBM * kSlab;        // 32 KiB
+constexpr int kStageBytes = 2 * kOperandStage;    // A + B = 64 KiB
+constexpr int kStages = 2;
+constexpr int kLoadsPerOperand = kOperandStage / 1024 / 4;  // per wave: 8
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kGroupM = 8;
 constexpr int kNumXcd = 8;
@@ -129,21 +131,29 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
 }
 
 // Per-input-type MFMA shape.  The wave's 128 x 128 accumulator is NB x NB
-// blocks of BLK x BLK.  A wave reads 16 fragments of 16 bytes per slab,
-// 0..7 for A and 8..15 for B.  Fragment r of an operand sits at
-//   base[r & 1] + r_stride * (r >> 1)        (base: lane-dependent VGPR)
-// so all reads use immediate offsets from at most two base registers.
+// blocks of BLK x BLK.  A wave reads 16 fragments of 16 bytes per half
+// slab (8 of A, 8 of B), all at immediate offsets from at most two base
+// registers per operand.
 template <int IN>
 struct Mma;
 
 // 16 x 16 shapes (bf16, fp32): read r of an operand covers rows 16r +
-// lane%16 of the wave's 128 rows and chunk lane/16.
+// lane%16 of the wave's 128 rows and chunk lane/16 of the half slab.
 struct Mma16Base {
   static constexpr int BLK = 16, NB = 8, R = 4;
   typedef f32x4 Acc;
-  static constexpr int kPairStride = 2 * 16 * kSlab;  // reads r and r+2 are 32 rows apart
-  __device__ static int base_row(int lane, int odd) { return 16 * odd + (lane & 15); }
+  typedef i32x4 Frags[16];  // 0..7: A blocks, 8..15: B blocks
+  // reads r and r+1 are 16 rows (two 8-row LDS blocks) apart
+  static constexpr int kReadStride = 2 * 1024;
+  __device__ static int base_row(int lane, int odd) { return lane & 15; }
   __device__ static int base_chunk(int lane, int odd) { return lane >> 4; }
+  __device__ static void read(const uint8_t* half_base, const int (&fb)[4], Frags& F) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      F[r] = *reinterpret_cast<const i32x4*>(half_base + fb[0] + kReadStride * r);
+      F[8 + r] = *reinterpret_cast<const i32x4*>(half_base + fb[2] + kReadStride * r);
+    }
+  }
   // MFMA 16 x 16 result: lane holds column lane%16, rows 4*(lane/16) + r
   __device__ static int out_row(int i, int r, int lane) { return 16 * i + 4 * (lane >> 4) + r; }
   __device__ static int out_col(int j, int lane) { return 16 * j + (lane & 15); }
@@ -151,7 +161,7 @@ struct Mma16Base {
 
 template <>
 struct Mma<IN_BF16> : Mma16Base {
-  __device__ static void mma(const i32x4 (&F)[16], Acc (&acc)[NB][NB]) {
+  __device__ static void mma(const Frags& F, Acc (&acc)[NB][NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -166,7 +176,7 @@ template <>
 struct Mma<IN_F32> : Mma16Base {
   // The lane's 4 floats of a block are K values 4*(lane/16) + t; MFMA t
   // takes lane group lane/16 as its K index 0..3, identically for A and B.
-  __device__ static void mma(const i32x4 (&F)[16], Acc (&acc)[NB][NB]) {
+  __device__ static void mma(const Frags& F, Acc (&acc)[NB][NB]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -185,9 +195,22 @@ struct Mma<IN_F32> : Mma16Base {
 struct Mma32Base {
   static constexpr int BLK = 32, NB = 4, R = 16;
   typedef f32x16 Acc;
-  static constexpr int kPairStride = 32 * kSlab;
+  typedef i32x8 Frags[8];  // 0..3: A blocks, 4..7: B blocks (32 bytes per lane)
+  // block r/2 is 32 rows (four 8-row LDS blocks) further on
+  static constexpr int kReadStride = 4 * 1024;
   __device__ static int base_row(int lane, int odd) { return lane & 31; }
   __device__ static int base_chunk(int lane, int odd) { return 2 * (lane >> 5) + odd; }
+  __device__ static void read(const uint8_t* half_base, const int (&fb)[4], Frags& F) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const i32x4 a0 = *reinterpret_cast<const i32x4*>(half_base + fb[0] + kReadStride * b);
+      const i32x4 a1 = *reinterpret_cast<const i32x4*>(half_base + fb[1] + kReadStride * b);
+      const i32x4 b0 = *reinterpret_cast<const i32x4*>(half_base + fb[2] + kReadStride * b);
+      const i32x4 b1 = *reinterpret_cast<const i32x4*>(half_base + fb[3] + kReadStride * b);
+      F[b] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      F[4 + b] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
   // MFMA 32 x 32 result: lane holds column lane%32, rows 8*(r/4) + 4*(lane/32) + r%4
   __device__ static int out_row(int i, int r, int lane) {
     return 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -197,82 +220,79 @@ struct Mma32Base {
 
 template <>
 struct Mma<IN_E4M3> : Mma32Base {
-  __device__ static void mma(const i32x4 (&F)[16], Acc (&acc)[NB][NB]) {
+  __device__ static void mma(const Frags& F, Acc (&acc)[NB][NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const i32x8 a = __builtin_shufflevector(F[2 * i], F[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const i32x8 b =
-            __builtin_shufflevector(F[8 + 2 * j], F[8 + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int j = 0; j < NB; ++j)
         // formats 0/0 = e4m3 for A and B; E8M0 scale 127 = 2^0
-        acc[i][j] =
-            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 127, 0, 127);
-      }
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F[i], F[NB + j], acc[i][j], 0,
+                                                                    0, 0, 127, 0, 127);
   }
 };
 
 // Tile-invariant addressing of one workgroup.
+//
+// LDS layout of one operand in a stage: 32 blocks of 8 rows x 128 bytes,
+// block b at b * 1 KiB; inside a block, half h (bytes 64h..64h+63 of each
+// row) at + 512 h, row r % 8 at + 64 (r % 8), and logical 16-byte chunk q
+// of the half at + 16 (q ^ f(r)).  One DMA instruction fills one block:
+// lane l takes half l/32, row (l/4) % 8 and stored chunk l % 4, so every
+// row's whole 128-byte line is read by one instruction.
 struct TileCtx {
   const uint8_t* Ab;
   const uint8_t* Bb;
   uint32_t a_bytes, b_bytes;  // valid rows * row bytes
-  uint32_t ga[kLoadsPerOperand], gb[kLoadsPerOperand];  // per-lane global offsets
-  uint32_t gk;                // lane's K byte offset within a slab
+  uint32_t ga[2], gb[2];      // per-lane global offsets for even / odd blocks
+  uint32_t lda16, ldb16;      // 16 rows of A / B in bytes (block pair stride)
+  uint32_t gk[2];             // lane's K byte offset within a slab, even / odd blocks
   int kbytes;
-  int fill;                   // wave's LDS fill offset within a stage (uniform)
+  int fill;                   // wave's first LDS block within an operand stage
+  int KT;
 };
 
 __device__ __forceinline__ void issue_slab(const TileCtx& c, uint8_t* smem, int kt, int stage) {
   const uint32_t k0b = static_cast<uint32_t>(kt) * kSlab;
-  const uint32_t kinv = (static_cast<int>(k0b + c.gk) < c.kbytes) ? 0u : kOutOfRange;
+  // chunks past K: top offset bit set, so the load is out of range (zeros)
+  uint32_t kinv[2];
+#pragma unroll
+  for (int odd = 0; odd < 2; ++odd)
+    kinv[odd] = (static_cast<int>(k0b + c.gk[odd]) < c.kbytes) ? 0u : kOutOfRange;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(c.Ab + k0b, c.a_bytes - k0b);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(c.Bb + k0b, c.b_bytes - k0b);
   uint8_t* sA = smem + stage * kStageBytes + c.fill;
   uint8_t* sB = sA + kOperandStage;
 #pragma unroll
   for (int i = 0; i < kLoadsPerOperand; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(sA + 1024 * i), 16, c.ga[i] | kinv,
-                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rA, (lds_ptr_t)(sA + 1024 * i), 16, (c.ga[i & 1] + (i >> 1) * c.lda16) | kinv[i & 1], 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < kLoadsPerOperand; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(sB + 1024 * i), 16, c.gb[i] | kinv,
-                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rB, (lds_ptr_t)(sB + 1024 * i), 16, (c.gb[i & 1] + (i >> 1) * c.ldb16) | kinv[i & 1], 0, 0, 0);
 }
 
-template <int IN>
-__device__ __forceinline__ void read_frags(const uint8_t* stage_base, const int (&fb)[4],
-                                           i32x4 (&F)[16]) {
-  using M = Mma<IN>;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    F[r] = *reinterpret_cast<const i32x4*>(stage_base + fb[r & 1] + M::kPairStride * (r >> 1));
-    F[8 + r] =
-        *reinterpret_cast<const i32x4*>(stage_base + fb[2 + (r & 1)] + M::kPairStride * (r >> 1));
-  }
-}
-
-// Wait until this wave's loads of a slab are complete when `after` more
-// slabs were issued behind it.
-__device__ __forceinline__ void wait_slab(int after) {
-  if (after >= 3) wait_vmcnt<3 * kLoadsPerSlab>();
-  else if (after == 2) wait_vmcnt<2 * kLoadsPerSlab>();
-  else if (after == 1) wait_vmcnt<kLoadsPerSlab>();
-  else wait_vmcnt<0>();
-}
-
-// One pipeline step: slab kt's fragments are being read into Fcur; slabs
-// kt+1 .. min(KT-1, kt+3) are in flight to LDS.
-template <int IN>
+// One half-slab step j (stage j/2 % 2, half j % 2).  Fcur holds (or is
+// receiving) half j's fragments.  Odd steps end a stage: after the barrier
+// every wave holds both halves of it in registers, so the next-but-one slab
+// can be loaded into it, and the next slab (issued one stage ago) is complete.
+template <int IN, bool ODD>
 __device__ __forceinline__ void pipeline_step(const TileCtx& c, uint8_t* smem, const int (&fb)[4],
-                                              int kt, int KT, i32x4 (&Fcur)[16],
-                                              i32x4 (&Fnext)[16],
+                                              int j, int J, typename Mma<IN>::Frags& Fcur,
+                                              typename Mma<IN>::Frags& Fnext,
                                               typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB]) {
+  const int kt = j >> 1;
   wait_lgkmcnt0();
-  if (kt + 1 < KT) wait_slab(min(KT - 1, kt + kStages - 1) - (kt + 1));
-  __syncthreads();
-  if (kt + kStages < KT) issue_slab(c, smem, kt + kStages, kt % kStages);
-  if (kt + 1 < KT) read_frags<IN>(smem + ((kt + 1) % kStages) * kStageBytes, fb, Fnext);
+  if constexpr (ODD) {
+    if (j + 1 < J) {
+      wait_vmcnt<0>();  // slab kt+1 (the only slab in flight) has landed
+      __syncthreads();
+      if (kt + kStages < c.KT) issue_slab(c, smem, kt + kStages, kt % kStages);
+      Mma<IN>::read(smem + ((kt + 1) % kStages) * kStageBytes, fb, Fnext);
+    }
+  } else {
+    Mma<IN>::read(smem + (kt % kStages) * kStageBytes + 512, fb, Fnext);
+  }
   Mma<IN>::mma(Fcur, acc);
 }
 
@@ -302,30 +322,35 @@ gemm_tn_kernel(GemmParams p) {
   c.a_bytes = static_cast<uint32_t>(min(kBM, p.M - m0)) * lda_b;
   c.b_bytes = static_cast<uint32_t>(min(kBN, p.N - n0)) * ldb_b;
   c.kbytes = p.K * ES;
+  c.lda16 = 16 * lda_b;
+  c.ldb16 = 16 * ldb_b;
   const int KT = (c.kbytes + kSlab - 1) / kSlab;
+  c.KT = KT;
 
-  // Load mapping: wave instruction i fills LDS rows 16*(4*wave + i) .. +15;
-  // lane l writes row +l/4, stored chunk l%4, which holds global chunk
-  // (l%4) ^ f(row); f depends on row%16 = l/4 only.
-  const int lrow = lane >> 2;
-  const int gchunk = (lane & 3) ^ chunk_perm(lrow);
-  c.gk = gchunk * 16;
+  // DMA lane mapping.  Wave w fills blocks 8w .. 8w+7 of each operand
+  // stage; block b holds rows 8b .. 8b+7, so f(row) depends on b % 2 and
+  // on the lane's row within the block.
+  const int half = lane >> 5, brow = (lane >> 2) & 7, schunk = lane & 3;
 #pragma unroll
-  for (int i = 0; i < kLoadsPerOperand; ++i) {
-    c.ga[i] = (16 * (4 * wave + i) + lrow) * lda_b + c.gk;
-    c.gb[i] = (16 * (4 * wave + i) + lrow) * ldb_b + c.gk;
+  for (int odd = 0; odd < 2; ++odd) {
+    const int row = 64 * wave + 8 * odd + brow;          // row of block 8w + odd
+    const int gch = half * 4 + (schunk ^ chunk_perm(row));
+    c.ga[odd] = row * lda_b + gch * 16;
+    c.gb[odd] = row * ldb_b + gch * 16;
+    c.gk[odd] = gch * 16;
   }
-  c.fill = wave * 4 * 1024;
+  c.fill = wave * 8 * 1024;
 
   // Fragment base offsets within a stage: [A even, A odd, B even, B odd].
-  // f(row) depends on row % 16 = lane % 16 for every read of the lane.
-  const int perm = chunk_perm(lane & 15);
+  // Rows of every read of a lane agree mod 16 with the lane's base row.
   int fb[4];
 #pragma unroll
   for (int odd = 0; odd < 2; ++odd) {
-    const int chunk = (M::base_chunk(lane, odd) ^ perm) << 4;
-    fb[odd] = (wm * 128 + M::base_row(lane, odd)) * kSlab + chunk;
-    fb[2 + odd] = kOperandStage + (wn * 128 + M::base_row(lane, odd)) * kSlab + chunk;
+    const int ra = wm * 128 + M::base_row(lane, odd);
+    const int rb = wn * 128 + M::base_row(lane, odd);
+    const int q = M::base_chunk(lane, odd);
+    fb[odd] = (ra >> 3) * 1024 + (ra & 7) * 64 + ((q ^ chunk_perm(ra)) << 4);
+    fb[2 + odd] = kOperandStage + (rb >> 3) * 1024 + (rb & 7) * 64 + ((q ^ chunk_perm(rb)) << 4);
   }
 
   typename M::Acc acc[M::NB][M::NB];
@@ -334,17 +359,20 @@ gemm_tn_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < M::NB; ++j) acc[i][j] = typename M::Acc{};
 
-  i32x4 F0[16], F1[16];
+  typename M::Frags F0, F1;
 
-  // Prologue: slabs 0..3 in flight, slab 0's fragments requested.
-  for (int t = 0; t < kStages && t < KT; ++t) issue_slab(c, smem, t, t);
-  wait_slab(min(KT - 1, kStages - 1));
+  // Prologue: slabs 0 and 1 in flight, slab 0 complete, half 0 requested.
+  issue_slab(c, smem, 0, 0);
+  if (KT > 1) issue_slab(c, smem, 1, 1);
+  if (KT > 1) wait_vmcnt<2 * kLoadsPerOperand>();
+  else wait_vmcnt<0>();
   __syncthreads();
-  read_frags<IN>(smem, fb, F0);
+  M::read(smem, fb, F0);
 
-  for (int kt = 0; kt < KT; kt += 2) {
-    pipeline_step<IN>(c, smem, fb, kt, KT, F0, F1, acc);
-    if (kt + 1 < KT) pipeline_step<IN>(c, smem, fb, kt + 1, KT, F1, F0, acc);
+  const int J = 2 * KT;  // half slabs
+  for (int j = 0; j < J; j += 2) {
+    pipeline_step<IN, false>(c, smem, fb, j, J, F0, F1, acc);
+    pipeline_step<IN, true>(c, smem, fb, j + 1, J, F1, F0, acc);
   }
 
   // Epilogue: D = alpha * acc + beta * C, through a per-wave base pointer.
@@ -380,7 +408,7 @@ gemm_tn_kernel(GemmParams p) {
 }
 
 template <int IN, int OUT>
-hipError_t launch_t(const GemmParams& p, hipStream_t stream) {
+inline hipError_t launch_t(const GemmParams& p, hipStream_t stream) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = (p.N + kBN - 1) / kBN;
   const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
@@ -389,16 +417,5 @@ hipError_t launch_t(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm(int in_kind, int out_kind, const GemmParams& p, hipStream_t stream) {
-  if (p.M <= 0 || p.N <= 0 || p.L <= 0) return hipSuccess;
-  if (in_kind == IN_F32 && out_kind == OUT_F32) return launch_t<IN_F32, OUT_F32>(p, stream);
-  if (in_kind == IN_BF16 && out_kind == OUT_F32) return launch_t<IN_BF16, OUT_F32>(p, stream);
-  if (in_kind == IN_BF16 && out_kind == OUT_BF16) return launch_t<IN_BF16, OUT_BF16>(p, stream);
-  if (in_kind == IN_E4M3 && out_kind == OUT_BF16) return launch_t<IN_E4M3, OUT_BF16>(p, stream);
-  if (in_kind == IN_E4M3 && out_kind == OUT_F32) return launch_t<IN_E4M3, OUT_F32>(p, stream);
-  return hipErrorInvalidValue;
-}
-
+}  // namespace tile
 }  // namespace dg

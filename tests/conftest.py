@@ -11,8 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     # load what is built; build only when nothing is
-    lib = os.path.join(ROOT, "communication_tensor_gemm_amd", "libdistgemm.so")
-    if not os.path.exists(lib):
+    pkg = os.path.join(ROOT, "communication_tensor_gemm_amd")
+    lib = os.path.join(pkg, "libdistgemm.so")
+    if os.path.isdir(pkg) and not os.path.exists(lib):
         from communication_tensor_gemm_amd.build import build
         build()
 
