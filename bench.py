@@ -126,8 +126,10 @@ def parity_spot_check(w, x, D):
 
 
 KERNEL_SOURCES = ["communication_tensor_gemm_amd/csrc/gemm_tile.h",
+                  "communication_tensor_gemm_amd/csrc/gemm_launch.h",
                   "communication_tensor_gemm_amd/csrc/gemm_mfma16.hip",
-                  "communication_tensor_gemm_amd/csrc/gemm_mfma_f8.hip"]
+                  "communication_tensor_gemm_amd/csrc/gemm_mfma_f8.hip",
+                  "communication_tensor_gemm_amd/build.py"]
 TRAFFIC_FILE = "profiles/gemm_tn_kernel_hbm_traffic.txt"
 
 

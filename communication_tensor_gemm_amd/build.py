@@ -18,9 +18,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gemm_mfma16.hip", "gemm_mfma_f8.hip", "distgemm.hip"]
 # per-source extra flags
 EXTRA = {
-    # 16 x 16 MFMA family: accumulators in VGPR form, or the compiler spills
-    # the fragment buffers; the e4m3 family spills under that form instead
-    "gemm_mfma16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the fp32 half slab is 256 MFMAs long; without a higher threshold the
+    # unroller gives up and the accumulators become a stack array
+    "gemm_mfma16.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"],
 }
 ARCH = "gfx950"
 

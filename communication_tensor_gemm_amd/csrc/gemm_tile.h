@@ -4,34 +4,44 @@
 //
 // Tiling.  A workgroup of 256 threads (4 wave64s, one per SIMD) owns a
 // 256 x 256 tile of D; the waves form a 2 x 2 grid and each holds a
-// 128 x 128 fp32 accumulator in 256 AGPRs.  K is walked in slabs of 64
-// bytes per operand row (32 bf16, 64 e4m3 or 16 fp32 values), so one LDS
-// geometry serves every input type and only the MFMA differs:
-//   bf16 : v_mfma_f32_16x16x32_bf16         (8 x 8 blocks of 16 x 16)
-//   fp32 : v_mfma_f32_16x16x4_f32           (8 x 8 blocks of 16 x 16)
-//   e4m3 : v_mfma_scale_f32_32x32x64_f8f6f4 (4 x 4 blocks of 32 x 32,
-//          neutral E8M0 block scales; per-tensor scales go to the epilogue)
+// 128 x 128 fp32 accumulator in all 256 of its AGPRs.  K is walked in slabs
+// of 128 bytes per operand row (64 bf16, 128 e4m3 or 32 fp32 values), each
+// multiplied in two half slabs of 64 bytes, so one LDS geometry serves every
+// input type and only the MFMA differs:
+//   bf16 : v_mfma_f32_16x16x32_bf16    (8 x 8 blocks of 16 x 16,   64 per half slab)
+//   fp32 : v_mfma_f32_16x16x4_f32      (8 x 8 blocks x 4 K steps, 256 per half slab)
+//   e4m3 : v_mfma_f32_32x32x64_f8f6f4  (4 x 4 blocks of 32 x 32,   16 per half slab;
+//          per-tensor scales are applied in the epilogue)
 //
 // Data movement.  Both operands are K-contiguous ("TN"), so a lane's MFMA
-// fragment is 16 contiguous bytes of one row (ds_read_b128).  K is walked in
-// slabs of 128 bytes per row (one cache line), moved from global memory
-// straight into LDS with buffer_load_dwordx4 ... lds: each wave instruction
-// fills 1 KiB of LDS (lane l -> bytes 16l..16l+15), eight whole rows, so the
-// L1 asks L2 for full 128-byte lines (64-byte requests halve the bytes per
-// outstanding request and measured about half the L2 -> LDS rate).  Within a
+// fragment is 16 contiguous bytes of one row (ds_read_b128).  Operand slabs
+// go from global memory straight into LDS with buffer_load_dwordx4 ... lds:
+// each wave instruction fills 1 KiB of LDS (lane l -> bytes 16l..16l+15),
+// eight whole 128-byte rows, so the L1 asks L2 for full lines.  Within a
 // 64-byte half row the four 16-byte chunks of row r are stored XOR-permuted
-// by f(r) = ((r>>1) ^ (r>>2)) & 3, which puts the 16 rows that 16 lanes read
-// in one LDS cycle on distinct banks (zero bank conflicts measured).  The
-// buffer descriptor of each operand covers only the tile's valid rows, so
-// rows past M or N load as zeros (out-of-range lanes of an LDS load write
-// zeros), and chunks past K are pushed out of range by the offset's top bit.
+// by f(r) = ((r>>1) ^ (r>>2)) & 3, which puts the rows that one LDS cycle
+// serves on distinct banks (zero bank conflicts measured).  The buffer
+// descriptor of each operand covers only the tile's valid rows, so rows past
+// M or N load as zeros (out-of-range lanes of an LDS load write zeros), and
+// chunks past K are pushed out of range by the offset's top bit.
 //
-// Pipeline.  Two LDS stages of 64 KiB (A and B slabs).  MFMAs walk half
-// slabs; fragments of the next half slab are read while the current one is
-// multiplied.  At the end of each slab one barrier certifies that every
-// wave holds the slab in registers and that the next slab has landed; the
-// slab after next is then loaded into the stage just vacated, so loads run
-// one slab (about 2000 MFMA cycles) ahead.
+// Pipeline.  LDS holds a ring of five 32 KiB operand slabs (160 KiB): A(kt)
+// in slot 2kt mod 5, B(kt) in slot 2kt+1 mod 5.  While slab kt is being
+// multiplied, slab kt+1 is resident and A(kt+2) is in flight.  One barrier
+// per slab (at the start of its second half) certifies that every wave holds
+// slab kt in registers and that slab kt+1 has landed; it is a bare s_barrier
+// after an explicit s_waitcnt, because the fence of __syncthreads() would
+// wait for every outstanding LDS load, A(kt+2) included.
+//
+// Issue order.  With one wave per SIMD, any instruction the wave issues
+// between MFMAs that the MFMA pipe has not covered is idle matrix time, so
+// each half slab is written as a fixed sequence: its MFMAs, with the
+// fragment reads of the next half slab and the DMA loads of the slab being
+// prefetched placed after given MFMAs (scheduling barriers keep that order).
+// The MFMAs are inline asm with the accumulator tied to an AGPR, which keeps
+// all 64 accumulator blocks in place across the loop; with the builtin the
+// compiler copied accumulators between MFMAs (about 100 to 400 moves per
+// slab) and the kernel ran at about half the MFMA rate.
 //
 // Workgroup -> tile mapping is XCD-aware: MI355X places workgroup b on XCD
 // b mod 8, so each XCD gets one contiguous range of the tile order, and
@@ -46,24 +56,22 @@
 namespace dg {
 namespace tile {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kThreads = 256;
-constexpr int kSlab = 128;                        // bytes of K per operand row per stage
-constexpr int kHalf = 64;                         // fragment reads walk half slabs
-constexpr int kOperandStage = kBM * kSlab;        // 32 KiB
-constexpr int kStageBytes = 2 * kOperandStage;    // A + B = 64 KiB
-constexpr int kStages = 2;
-constexpr int kLoadsPerOperand = kOperandStage / 1024 / 4;  // per wave: 8
+constexpr int kSlab = 128;                        // bytes of K per operand row per slab
+constexpr int kOperandSlab = kBM * kSlab;         // 32 KiB
+constexpr int kSlots = 5;                         // LDS ring of operand slabs: 160 KiB
+constexpr int kLoadsPerOperand = kOperandSlab / 1024 / 4;  // per wave: 8
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kGroupM = 8;
 constexpr int kNumXcd = 8;
 
 static_assert(kBM == 256 && kBN == 256, "tile geometry");
+static_assert(kRowBytes == kSlab, "slab width");
 
 template <int IN>
 constexpr int elem_size() {
@@ -111,6 +119,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
+// Workgroup barrier without a memory fence: the caller has already waited
+// for what the other waves must see (its LDS loads, its fragment reads).
+// gfx950 does not drain memory counters at s_barrier; the "memory" clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -138,10 +151,13 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
   }
 }
 
-// Per-input-type MFMA shape.  The wave's 128 x 128 accumulator is NB x NB
-// blocks of BLK x BLK.  A wave reads 16 fragments of 16 bytes per half
-// slab (8 of A, 8 of B), all at immediate offsets from at most two base
-// registers per operand.
+// Per-input-type MFMA shape and issue schedule.  The wave's 128 x 128
+// accumulator is NB x NB blocks of BLK x BLK.  A half slab takes kMfma
+// MFMAs and kReads fragment reads of 16 bytes per lane.  Within a half slab,
+// fragment read q follows MFMA kReadAt + (q / kReadsPer) * kReadEvery and
+// DMA load d follows MFMA kDmaAt + d * kDmaEvery; both end early enough for
+// the reads to land before the next half slab and for the loads to keep
+// their lead.
 template <int IN>
 struct Mma;
 
@@ -149,19 +165,21 @@ struct Mma;
 // lane%16 of the wave's 128 rows and chunk lane/16 of the half slab.
 struct Mma16Base {
   static constexpr int BLK = 16, NB = 8, R = 4;
-  static constexpr bool kSplitDma = true;   // A and B bursts half a slab apart
+  static constexpr int kReads = 16;
   typedef f32x4 Acc;
   typedef i32x4 Frags[16];  // 0..7: A blocks, 8..15: B blocks
   // reads r and r+1 are 16 rows (two 8-row LDS blocks) apart
   static constexpr int kReadStride = 2 * 1024;
   __device__ static int base_row(int lane, int odd) { return lane & 15; }
   __device__ static int base_chunk(int lane, int odd) { return lane >> 4; }
-  __device__ static void read(const uint8_t* half_base, const int (&fb)[4], Frags& F) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      F[r] = *reinterpret_cast<const i32x4*>(half_base + fb[0] + kReadStride * r);
-      F[8 + r] = *reinterpret_cast<const i32x4*>(half_base + fb[2] + kReadStride * r);
-    }
+  // read q: A block q/2 (q even) or B block q/2 (q odd)
+  __device__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+                              Frags& F) {
+    const int r = q >> 1;
+    if ((q & 1) == 0)
+      F[r] = *reinterpret_cast<const i32x4*>(a + fb[0] + kReadStride * r);
+    else
+      F[8 + r] = *reinterpret_cast<const i32x4*>(b + fb[2] + kReadStride * r);
   }
   // MFMA 16 x 16 result: lane holds column lane%16, rows 4*(lane/16) + r
   __device__ static int out_row(int i, int r, int lane) { return 16 * i + 4 * (lane >> 4) + r; }
@@ -170,58 +188,56 @@ struct Mma16Base {
 
 template <>
 struct Mma<IN_BF16> : Mma16Base {
-  __device__ static void mma(const Frags& F, Acc (&acc)[NB][NB]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, F[i]), __builtin_bit_cast(bf16x8, F[8 + j]), acc[i][j], 0,
-            0, 0);
+  static constexpr int kMfma = 64;
+  static constexpr int kReadAt = 1, kReadEvery = 2, kReadsPer = 1;
+  static constexpr int kDmaAt = 2, kDmaEvery = 8;
+  // MFMA m: block (m / 8, m % 8)
+  __device__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
+    const int i = m >> 3, j = m & 7;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc[i][j])
+                 : "v"(F[i]), "v"(F[8 + j]));
   }
 };
 
 template <>
 struct Mma<IN_F32> : Mma16Base {
-  // The lane's 4 floats of a block are K values 4*(lane/16) + t; MFMA t
-  // takes lane group lane/16 as its K index 0..3, identically for A and B.
-  __device__ static void mma(const Frags& F, Acc (&acc)[NB][NB]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const f32x4 a = __builtin_bit_cast(f32x4, F[i]);
-          const f32x4 b = __builtin_bit_cast(f32x4, F[8 + j]);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc[i][j], 0, 0, 0);
-        }
+  static constexpr int kMfma = 256;
+  static constexpr int kReadAt = 1, kReadEvery = 4, kReadsPer = 1;
+  static constexpr int kDmaAt = 2, kDmaEvery = 8;
+  // MFMA m: K step t = m / 64 of block ((m / 8) % 8, m % 8).  The lane's 4
+  // floats of a block are K values 4*(lane/16) + t; the 16x16x4 MFMA takes
+  // lane group lane/16 as its K index, identically for A and B.
+  __device__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
+    const int t = m >> 6, i = (m >> 3) & 7, j = m & 7;
+    const float a = __builtin_bit_cast(f32x4, F[i])[t];
+    const float b = __builtin_bit_cast(f32x4, F[8 + j])[t];
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(a), "v"(b));
   }
 };
 
-// 32 x 32 shapes: read r of an operand covers block r/2 (rows 32*(r/2) +
-// lane%32) and chunk 2*(lane/32) + r%2: 32 contiguous bytes per lane per block.
+// 32 x 32 shape (e4m3): read r of an operand covers block r/2 (rows 32*(r/2)
+// + lane%32) and chunk 2*(lane/32) + r%2: 32 contiguous bytes per lane per
+// block, read as two 16-byte halves.
 struct Mma32Base {
   static constexpr int BLK = 32, NB = 4, R = 16;
-  // one DMA burst per slab: the split measured 9% slower for e4m3 (1638 vs
-  // 1795 TFLOP/s at 8192 x 13312 x 16384), 21% faster for bf16
-  static constexpr bool kSplitDma = false;
+  static constexpr int kReads = 16;
   typedef f32x16 Acc;
   typedef i32x8 Frags[8];  // 0..3: A blocks, 4..7: B blocks (32 bytes per lane)
-  // block r/2 is 32 rows (four 8-row LDS blocks) further on
+  // block b is 32 rows (four 8-row LDS blocks) further on
   static constexpr int kReadStride = 4 * 1024;
   __device__ static int base_row(int lane, int odd) { return lane & 31; }
   __device__ static int base_chunk(int lane, int odd) { return 2 * (lane >> 5) + odd; }
-  __device__ static void read(const uint8_t* half_base, const int (&fb)[4], Frags& F) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const i32x4 a0 = *reinterpret_cast<const i32x4*>(half_base + fb[0] + kReadStride * b);
-      const i32x4 a1 = *reinterpret_cast<const i32x4*>(half_base + fb[1] + kReadStride * b);
-      const i32x4 b0 = *reinterpret_cast<const i32x4*>(half_base + fb[2] + kReadStride * b);
-      const i32x4 b1 = *reinterpret_cast<const i32x4*>(half_base + fb[3] + kReadStride * b);
-      F[b] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      F[4 + b] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+  // read q: block q/4 of A (q%4 < 2) or B, half q%2 of its 32 bytes
+  __device__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+                              Frags& F) {
+    const int blk = q >> 2, op = (q >> 1) & 1, h = q & 1;
+    const i32x4 v = *reinterpret_cast<const i32x4*>((op ? b : a) + fb[2 * op + h] +
+                                                    kReadStride * blk);
+    if (h == 0)
+      F[4 * op + blk].lo = v;
+    else
+      F[4 * op + blk].hi = v;
   }
   // MFMA 32 x 32 result: lane holds column lane%32, rows 8*(r/4) + 4*(lane/32) + r%4
   __device__ static int out_row(int i, int r, int lane) {
@@ -232,25 +248,26 @@ struct Mma32Base {
 
 template <>
 struct Mma<IN_E4M3> : Mma32Base {
-  __device__ static void mma(const Frags& F, Acc (&acc)[NB][NB]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        // formats 0/0 = e4m3 for A and B; E8M0 scale 127 = 2^0
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F[i], F[NB + j], acc[i][j], 0,
-                                                                    0, 0, 127, 0, 127);
+  static constexpr int kMfma = 16;
+  static constexpr int kReadAt = 0, kReadEvery = 1, kReadsPer = 2;
+  static constexpr int kDmaAt = 0, kDmaEvery = 1;
+  // MFMA m: block (m / 4, m % 4); format fields 0/0 select e4m3 for A and B
+  __device__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
+    const int i = m >> 2, j = m & 3;
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                 : "+a"(acc[i][j])
+                 : "v"(F[i]), "v"(F[NB + j]));
   }
 };
 
 // Tile-invariant addressing of one workgroup.
 //
-// LDS layout of one operand in a stage: 32 blocks of 8 rows x 128 bytes,
-// block b at b * 1 KiB; inside a block, half h (bytes 64h..64h+63 of each
-// row) at + 512 h, row r % 8 at + 64 (r % 8), and logical 16-byte chunk q
-// of the half at + 16 (q ^ f(r)).  One DMA instruction fills one block:
-// lane l takes half l/32, row (l/4) % 8 and stored chunk l % 4, so every
-// row's whole 128-byte line is read by one instruction.
+// LDS layout of one operand slab: 32 blocks of 8 rows x 128 bytes, block b
+// at b * 1 KiB; inside a block, half h (bytes 64h..64h+63 of each row) at
+// + 512 h, row r % 8 at + 64 (r % 8), and logical 16-byte chunk q of the half
+// at + 16 (q ^ f(r)).  One DMA instruction fills one block: lane l takes half
+// l/32, row (l/4) % 8 and stored chunk l % 4, so every row's whole 128-byte
+// line is read by one instruction.
 struct TileCtx {
   const uint8_t* Ab;
   const uint8_t* Bb;
@@ -259,75 +276,74 @@ struct TileCtx {
   uint32_t lda16, ldb16;      // 16 rows of A / B in bytes (block pair stride)
   uint32_t gk[2];             // lane's K byte offset within a slab, even / odd blocks
   int kbytes;
-  int fill;                   // wave's first LDS block within an operand stage
-  int KT;
+  int fill;                   // wave's first LDS block within an operand slab
 };
 
-// Issue the DMA of one operand (OP 0: A, 1: B, 2: both) of slab kt into `stage`.
+__device__ __forceinline__ int slot_add(int s, int d) {
+  s += d;
+  return s >= kSlots ? s - kSlots : s;
+}
+
+// DMA state of one operand slab (OP 0: A, 1: B) of slab kt bound for a ring slot.
 template <int OP>
-__device__ __forceinline__ void issue_slab(const TileCtx& c, uint8_t* smem, int kt, int stage) {
-  const uint32_t k0b = static_cast<uint32_t>(kt) * kSlab;
-  // chunks past K: top offset bit set, so the load is out of range (zeros)
+struct SlabLoad {
+  __amdgpu_buffer_rsrc_t r;
   uint32_t kinv[2];
+  uint8_t* dst;
+  __device__ __forceinline__ SlabLoad(const TileCtx& c, uint8_t* smem, int kt, int slot) {
+    const uint32_t k0b = static_cast<uint32_t>(kt) * kSlab;
+    // chunks past K: top offset bit set, so the load is out of range (zeros)
 #pragma unroll
-  for (int odd = 0; odd < 2; ++odd)
-    kinv[odd] = (static_cast<int>(k0b + c.gk[odd]) < c.kbytes) ? 0u : kOutOfRange;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(c.Ab + k0b, c.a_bytes - k0b);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(c.Bb + k0b, c.b_bytes - k0b);
-  uint8_t* sA = smem + stage * kStageBytes + c.fill;
-  uint8_t* sB = sA + kOperandStage;
-  if constexpr (OP != 1) {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(sA + 1024 * i), 16,
-                                               (c.ga[i & 1] + (i >> 1) * c.lda16) | kinv[i & 1], 0,
-                                               0, 0);
+    for (int odd = 0; odd < 2; ++odd)
+      kinv[odd] = (static_cast<int>(k0b + c.gk[odd]) < c.kbytes) ? 0u : kOutOfRange;
+    r = OP == 0 ? make_rsrc(c.Ab + k0b, c.a_bytes - k0b) : make_rsrc(c.Bb + k0b, c.b_bytes - k0b);
+    dst = smem + slot * kOperandSlab + c.fill;
   }
-  if constexpr (OP != 0) {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(sB + 1024 * i), 16,
-                                               (c.gb[i & 1] + (i >> 1) * c.ldb16) | kinv[i & 1], 0,
-                                               0, 0);
+  // load d of the wave's eight: LDS block fill/1K + d, rows 8d.. of the wave's 64
+  __device__ __forceinline__ void issue(const TileCtx& c, int d) const {
+    const uint32_t* g = OP == 0 ? c.ga : c.gb;
+    const uint32_t ld16 = OP == 0 ? c.lda16 : c.ldb16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024 * d), 16,
+                                             (g[d & 1] + (d >> 1) * ld16) | kinv[d & 1], 0, 0, 0);
   }
+};
+
+template <int OP>
+__device__ __forceinline__ void issue_operand(const TileCtx& c, uint8_t* smem, int kt, int slot) {
+  const SlabLoad<OP> L(c, smem, kt, slot);
+#pragma unroll
+  for (int d = 0; d < kLoadsPerOperand; ++d) L.issue(c, d);
 }
 
-// Main loop.  Slab kt lives in LDS stage kt % 2 and is multiplied in two
-// half steps.  Fragments of the next half slab are read while the current
-// one is multiplied (F0 holds half 0, F1 half 1).  At the end of each slab
-// one barrier certifies that every wave holds the slab in registers and that
-// the next slab has landed; the slab after next is then loaded into the
-// stage just vacated, so loads run one slab (about 2000 MFMA cycles) ahead.
-// In the 16 x 16 family a slab's DMA goes out in two bursts -- its A rows
-// right after that barrier, its B rows one half step later: issuing all 16
-// loads of every wave at the barrier made each CU ask L2 for 64 KiB at once
-// and measured about 20% slower.  The steady-state body has no branches, so
-// the fragment buffers keep fixed registers; the last two slabs are peeled.
-template <int IN>
-__device__ __forceinline__ void half0(const TileCtx& c, uint8_t* smem, const int (&fb)[4], int kt,
-                                      bool issue_b, typename Mma<IN>::Frags& F0,
-                                      typename Mma<IN>::Frags& F1,
-                                      typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB]) {
-  wait_lgkmcnt0();
-  if constexpr (Mma<IN>::kSplitDma)
-    if (issue_b) issue_slab<1>(c, smem, kt + 1, (kt + 1) & 1);
-  Mma<IN>::read(smem + (kt & 1) * kStageBytes + 512, fb, F1);
-  Mma<IN>::mma(F0, acc);
-}
-
-template <int IN>
-__device__ __forceinline__ void half1(const TileCtx& c, uint8_t* smem, const int (&fb)[4], int kt,
-                                      bool more, bool issue_next, typename Mma<IN>::Frags& F0,
-                                      typename Mma<IN>::Frags& F1,
-                                      typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB]) {
-  wait_lgkmcnt0();
-  if (more) {
-    wait_vmcnt<0>();  // slab kt+1, the only one in flight, has landed
-    __syncthreads();
-    if (issue_next) issue_slab<Mma<IN>::kSplitDma ? 0 : 2>(c, smem, kt + 2, kt & 1);
-    Mma<IN>::read(smem + ((kt + 1) & 1) * kStageBytes, fb, F0);
+// One half slab: the MFMAs on Fm, with (kRead) the reads of the next half
+// slab into Fr from LDS bases ra / rb and (kIssue) the DMA of operand kOp of
+// slab kt_issue into ring slot slot_issue, in the type's fixed order.
+template <int IN, bool kIssue, bool kRead, int kOp>
+__device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int kt_issue,
+                                          int slot_issue, const uint8_t* ra, const uint8_t* rb,
+                                          const int (&fb)[4], const typename Mma<IN>::Frags& Fm,
+                                          typename Mma<IN>::Frags& Fr,
+                                          typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB]) {
+  using M = Mma<IN>;
+  const SlabLoad<kOp> L(c, smem, kt_issue, slot_issue);
+#pragma unroll
+  for (int m = 0; m < M::kMfma; ++m) {
+    M::mma(m, Fm, acc);
+    if constexpr (kIssue) {
+      const int d = (m - M::kDmaAt) / M::kDmaEvery;
+      if (m >= M::kDmaAt && (m - M::kDmaAt) % M::kDmaEvery == 0 && d < kLoadsPerOperand)
+        L.issue(c, d);
+    }
+    if constexpr (kRead) {
+      const int g = (m - M::kReadAt) / M::kReadEvery;
+      if (m >= M::kReadAt && (m - M::kReadAt) % M::kReadEvery == 0) {
+#pragma unroll
+        for (int u = 0; u < M::kReadsPer; ++u)
+          if (g * M::kReadsPer + u < M::kReads) M::read(g * M::kReadsPer + u, ra, rb, fb, Fr);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  Mma<IN>::mma(F1, acc);
 }
 
 template <int IN, int OUT>
@@ -335,7 +351,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 gemm_tn_kernel(GemmParams p) {
   using M = Mma<IN>;
   constexpr int ES = elem_size<IN>();
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * kOperandSlab];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -359,10 +375,9 @@ gemm_tn_kernel(GemmParams p) {
   c.lda16 = 16 * lda_b;
   c.ldb16 = 16 * ldb_b;
   const int KT = (c.kbytes + kSlab - 1) / kSlab;
-  c.KT = KT;
 
   // DMA lane mapping.  Wave w fills blocks 8w .. 8w+7 of each operand
-  // stage; block b holds rows 8b .. 8b+7, so f(row) depends on b % 2 and
+  // slab; block b holds rows 8b .. 8b+7, so f(row) depends on b % 2 and
   // on the lane's row within the block.
   const int half = lane >> 5, brow = (lane >> 2) & 7, schunk = lane & 3;
 #pragma unroll
@@ -375,8 +390,8 @@ gemm_tn_kernel(GemmParams p) {
   }
   c.fill = wave * 8 * 1024;
 
-  // Fragment base offsets within a stage: [A even, A odd, B even, B odd].
-  // Rows of every read of a lane agree mod 16 with the lane's base row.
+  // Fragment base offsets within an operand slab: [A even, A odd, B even,
+  // B odd].  Rows of every read of a lane agree mod 16 with its base row.
   int fb[4];
 #pragma unroll
   for (int odd = 0; odd < 2; ++odd) {
@@ -384,7 +399,7 @@ gemm_tn_kernel(GemmParams p) {
     const int rb = wn * 128 + M::base_row(lane, odd);
     const int q = M::base_chunk(lane, odd);
     fb[odd] = (ra >> 3) * 1024 + (ra & 7) * 64 + ((q ^ chunk_perm(ra)) << 4);
-    fb[2 + odd] = kOperandStage + (rb >> 3) * 1024 + (rb & 7) * 64 + ((q ^ chunk_perm(rb)) << 4);
+    fb[2 + odd] = (rb >> 3) * 1024 + (rb & 7) * 64 + ((q ^ chunk_perm(rb)) << 4);
   }
 
   typename M::Acc acc[M::NB][M::NB];
@@ -395,34 +410,61 @@ gemm_tn_kernel(GemmParams p) {
 
   typename M::Frags F0, F1;
 
-  // Prologue: slab 0 and slab 1 in flight (slab 1's B rows are issued in
-  // slab 0's first half step when the DMA is split), slab 0 complete, its
-  // half 0 requested.
-  issue_slab<2>(c, smem, 0, 0);
-  if constexpr (M::kSplitDma) {
-    if (KT > 1) issue_slab<0>(c, smem, 1, 1);
-    if (KT > 1) wait_vmcnt<kLoadsPerOperand>();
-    else wait_vmcnt<0>();
+  // Prologue: A0, B0, A1, B1 into slots 0..3; slab 0 landed; its half 0 read.
+  issue_operand<0>(c, smem, 0, 0);
+  issue_operand<1>(c, smem, 0, 1);
+  if (KT > 1) {
+    issue_operand<0>(c, smem, 1, 2);
+    issue_operand<1>(c, smem, 1, 3);
+    wait_vmcnt<2 * kLoadsPerOperand>();
   } else {
-    if (KT > 1) issue_slab<2>(c, smem, 1, 1);
-    if (KT > 1) wait_vmcnt<2 * kLoadsPerOperand>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();
   }
-  __syncthreads();
-  M::read(smem, fb, F0);
+  barrier_only();
+#pragma unroll
+  for (int q = 0; q < M::kReads; ++q) M::read(q, smem, smem + kOperandSlab, fb, F0);
 
-  int kt = 0;
+  // Main loop, slab kt at ring position s (A(kt) in slot s, B(kt) in s+1):
+  //   half 0: MFMAs on F0 (half 0 of slab kt); read F1 = half 1 of slab kt;
+  //           prefetch A(kt+2) into slot s+4 (vacated by B(kt-1)).
+  //   half 1: wait until slab kt+1 has landed (A(kt+2) may still be in
+  //           flight) and F1 is in registers; barrier; MFMAs on F1; read
+  //           F0 = half 0 of slab kt+1; prefetch B(kt+2) into slot s
+  //           (vacated by A(kt)).
+  // A is loaded three half slabs ahead of its use and B two; the last two
+  // slabs are peeled so the steady-state body has no branches.
+  int kt = 0, s = 0;
   for (; kt + 2 < KT; ++kt) {
-    half0<IN>(c, smem, fb, kt, true, F0, F1, acc);
-    half1<IN>(c, smem, fb, kt, true, true, F0, F1, acc);
+    wait_lgkmcnt0();
+    half_step<IN, true, true, 0>(c, smem, kt + 2, slot_add(s, 4), smem + s * kOperandSlab + 512,
+                                 smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc);
+    wait_lgkmcnt0();
+    wait_vmcnt<kLoadsPerOperand>();
+    barrier_only();
+    half_step<IN, true, true, 1>(c, smem, kt + 2, s, smem + slot_add(s, 2) * kOperandSlab,
+                                 smem + slot_add(s, 3) * kOperandSlab, fb, F1, F0, acc);
+    s = slot_add(s, 2);
   }
-  if (kt + 1 < KT) {  // second to last slab: no slab after next
-    half0<IN>(c, smem, fb, kt, true, F0, F1, acc);
-    half1<IN>(c, smem, fb, kt, true, false, F0, F1, acc);
+  if (kt + 1 < KT) {  // second to last slab: nothing left to prefetch
+    wait_lgkmcnt0();
+    half_step<IN, false, true, 0>(c, smem, kt, s, smem + s * kOperandSlab + 512,
+                                  smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc);
+    wait_lgkmcnt0();
+    wait_vmcnt<0>();
+    barrier_only();
+    half_step<IN, false, true, 1>(c, smem, kt, s, smem + slot_add(s, 2) * kOperandSlab,
+                                  smem + slot_add(s, 3) * kOperandSlab, fb, F1, F0, acc);
+    s = slot_add(s, 2);
     ++kt;
   }
-  half0<IN>(c, smem, fb, kt, false, F0, F1, acc);  // last slab
-  half1<IN>(c, smem, fb, kt, false, false, F0, F1, acc);
+  wait_lgkmcnt0();  // last slab
+  half_step<IN, false, true, 0>(c, smem, kt, s, smem + s * kOperandSlab + 512,
+                                smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc);
+  wait_lgkmcnt0();
+  half_step<IN, false, false, 1>(c, smem, kt, s, smem, smem, fb, F1, F0, acc);
+  // The MFMAs are opaque to the compiler's hazard tracking: give the last
+  // ones their result latency before the epilogue reads the AGPRs.
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
 
   // Epilogue: D = alpha * acc + beta * C, through a per-wave base pointer.
   const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
