@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     dist_gemm_set_scales,
     dist_gemm_step_table,
     dist_gemm_step_times,
+    dist_gemm_step_timeline,
     lib,
 )

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdistgemm.so")
 SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_C": 3,
              "MONOLITHIC": 4}
 DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4}
-OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2}
+OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2, "COPY_STREAMS": 3,
+           "STEP_GROUP": 4}
 # bytes per element of (A/B, C/D) for each dtype
 ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
               "E4M3_F32": (1, 4)}
@@ -26,8 +27,8 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM",
 # C functions declared in include/distgemm.h (checked by the CPU tests)
 C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
                "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
-               "dist_gemm_step_times", "dist_gemm_destroy", "dist_gemm_last_error",
-               "dist_gemm_status_string")
+               "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_destroy",
+               "dist_gemm_last_error", "dist_gemm_status_string")
 
 
 class DistGemmError(RuntimeError):
@@ -66,6 +67,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     lib.dist_gemm_plan_steps.argtypes = [vp, ctypes.POINTER(Step), ctypes.POINTER(i32)]
     lib.dist_gemm_step_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.dist_gemm_step_timeline.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.dist_gemm_destroy.argtypes = [vp]
     lib.dist_gemm_last_error.argtypes = [vp]
     lib.dist_gemm_last_error.restype = ctypes.c_char_p
@@ -73,7 +75,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
     for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
                  "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
-                 "dist_gemm_step_times", "dist_gemm_destroy"):
+                 "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_destroy"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -154,6 +156,15 @@ def dist_gemm_step_times(plan) -> List[float]:
     return [buf[i] for i in range(n.value)]
 
 
+def dist_gemm_step_timeline(plan) -> List[tuple]:
+    """(copy_done_ms or -1, begin_ms, end_ms) per step of the last timed run."""
+    n = ctypes.c_int(0)
+    _check(lib.dist_gemm_step_timeline(plan, None, ctypes.byref(n)), plan)
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _check(lib.dist_gemm_step_timeline(plan, buf, ctypes.byref(n)), plan)
+    return [tuple(buf[3 * s + k] for k in range(3)) for s in range(n.value // 3)]
+
+
 def dist_gemm_destroy(plan):
     _check(lib.dist_gemm_destroy(plan))
 
@@ -178,6 +189,9 @@ class Plan:
 
     def step_times(self):
         return dist_gemm_step_times(self.handle)
+
+    def step_timeline(self):
+        return dist_gemm_step_timeline(self.handle)
 
     def _need(self, t, nbytes, name):
         if t is None or isinstance(t, int):

@@ -6,9 +6,10 @@
 // that arrives from a peer at every step is moved by the copy engine, not by
 // compute units, and each step's GEMM starts only after its operand is in
 // place.  On one GPU the peer's shard is a region of the caller's operand;
-// the copy engine here is SDMA (hipMemcpyDeviceToDeviceNoCU) on a side
-// stream, one copy per staged step, each followed by an event that the
-// step's GEMM launch waits on.  Step GEMMs alternate between the caller's
+// the copy engine here is SDMA (hipMemcpyDeviceToDeviceNoCU) on side
+// streams, one copy per staged step, each followed by an event that the
+// step's GEMM launch waits on.  Copies go round-robin to up to eight side
+// streams, one per peer link that the transfer stands in for.  Step GEMMs alternate between the caller's
 // stream and a second compute stream by step parity (the stream alternation
 // of the PyTorch symmetric-memory page's all-gather consumer), so the last,
 // partly filled wave of one step's workgroups can overlap the next step.
@@ -120,10 +121,15 @@ std::vector<dist_gemm_step> build_steps(const Problem& p) {
 }
 
 // Geometry of one staged shard: a 2-D region (height rows of width bytes,
-// src_pitch apart) of the source operand, copied densely into a slot.
+// src_pitch apart) of the source operand.  The staging buffer is height rows
+// of S-1 slots side by side: slot k occupies bytes [k*width, (k+1)*width) of
+// every staging row, and staging rows are (S-1)*width apart.  Consecutive
+// slots are therefore one contiguous region of every row, so the shards of
+// consecutive steps form one operand (or partial) matrix and their GEMMs can
+// run as one launch.
 struct CopyGeom {
   size_t width = 0, height = 0, src_pitch = 0;
-  size_t slot_bytes() const { return width * height; }
+  size_t staging_pitch(int slots) const { return width * static_cast<size_t>(slots); }
 };
 
 CopyGeom copy_geom(const Problem& p) {
@@ -164,17 +170,25 @@ struct dist_gemm_plan_s {
   CopyGeom geom;
   int device = 0;
   uint8_t* staging = nullptr;
-  size_t slot_stride = 0;
-  hipStream_t side = nullptr;  // copy engine stream
+  size_t staging_pitch = 0;  // bytes between staging rows: (S-1) slots of geom.width
+  std::vector<hipStream_t> sides;     // copy engine streams (created on demand)
+  std::vector<hipEvent_t> ev_side_done;  // one per side stream
   hipStream_t cs2 = nullptr;   // second compute stream
-  hipEvent_t ev_start = nullptr, ev_side_done = nullptr, ev_cs2_done = nullptr, ev_done = nullptr;
+  hipEvent_t ev_start = nullptr, ev_cs2_done = nullptr, ev_done = nullptr;
   std::vector<hipEvent_t> ev_copy;
   // Per-step timing ring: event pairs for the last `step_timing` runs,
   // indexed [run % step_timing][step].
   std::vector<hipEvent_t> t_begin, t_end;
+  // Timeline of the same runs: run start, and copy completion per step.
+  std::vector<hipEvent_t> t_run0, t_copy;
+  // [run % step_timing][step] = first step of the launch that computed it
+  // (launch events are recorded at that step's index).
+  std::vector<int> t_first;
   float scale_a = 1.0f, scale_b = 1.0f;
   int compute_streams = 2;
   int copy_engine = 0;
+  int copy_streams = 2;
+  int max_group = 2;  // consecutive staged steps per launch
   int step_timing = 0;
   int64_t timed_runs = 0;  // runs recorded since timing was (re)enabled
   bool has_prev = false;
@@ -197,15 +211,18 @@ int hip_fail(std::string* err, hipError_t e, const char* what) {
 
 void release(dist_gemm_plan_s* p) {
   if (!p) return;
-  if (p->side) (void)hipStreamSynchronize(p->side);
+  for (hipStream_t s : p->sides) if (s) (void)hipStreamSynchronize(s);
   if (p->cs2) (void)hipStreamSynchronize(p->cs2);
   if (p->ev_done) (void)hipEventSynchronize(p->ev_done);
   for (hipEvent_t e : p->ev_copy) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->t_begin) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->t_end) if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {p->ev_start, p->ev_side_done, p->ev_cs2_done, p->ev_done})
+  for (hipEvent_t e : p->t_run0) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->t_copy) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->ev_side_done) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {p->ev_start, p->ev_cs2_done, p->ev_done})
     if (e) (void)hipEventDestroy(e);
-  if (p->side) (void)hipStreamDestroy(p->side);
+  for (hipStream_t s : p->sides) if (s) (void)hipStreamDestroy(s);
   if (p->cs2) (void)hipStreamDestroy(p->cs2);
   if (p->staging) (void)hipFree(p->staging);
   delete p;
@@ -222,7 +239,25 @@ struct DeviceGuard {
   }
 };
 
-int enqueue_copy(dist_gemm_plan_s* P, const void* src_base, int shard, int slot) {
+// Make sure the plan owns at least n side streams (and their join events).
+int ensure_sides(dist_gemm_plan_s* P, int n, std::string* err) {
+  while (static_cast<int>(P->sides.size()) < n) {
+    hipStream_t s = nullptr;
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(err, e, "side stream creation");
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipStreamDestroy(s);
+      return hip_fail(err, e, "side stream event creation");
+    }
+    P->sides.push_back(s);
+    P->ev_side_done.push_back(ev);
+  }
+  return DIST_GEMM_OK;
+}
+
+int enqueue_copy(dist_gemm_plan_s* P, hipStream_t side, const void* src_base, int shard, int slot) {
   const CopyGeom& g = P->geom;
   const Problem& pr = P->pr;
   const uint8_t* src = static_cast<const uint8_t*>(src_base);
@@ -238,16 +273,42 @@ int enqueue_copy(dist_gemm_plan_s* P, const void* src_base, int shard, int slot)
     default:
       return DIST_GEMM_OK;
   }
-  uint8_t* dst = P->staging + static_cast<size_t>(slot) * P->slot_stride;
+  uint8_t* dst = P->staging + static_cast<size_t>(slot) * g.width;
   const hipMemcpyKind kind =
       P->copy_engine == 0 ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
   hipError_t e;
   if (g.height == 1)
-    e = hipMemcpyAsync(dst, src, g.width, kind, P->side);
+    e = hipMemcpyAsync(dst, src, g.width, kind, side);
   else
-    e = hipMemcpy2DAsync(dst, g.width, src, g.src_pitch, g.width, g.height, kind, P->side);
+    e = hipMemcpy2DAsync(dst, P->staging_pitch, src, g.src_pitch, g.width, g.height, kind, side);
   if (e != hipSuccess) return hip_fail(&P->err, e, "shard copy");
   return DIST_GEMM_OK;
+}
+
+// Launches of one run: consecutive staged steps whose shards are adjacent
+// (shard index and staging slot both one higher) merge, up to max_group
+// steps per launch; the unstaged step launches alone.
+struct LaunchGroup {
+  int first, count;
+};
+
+std::vector<LaunchGroup> group_steps(const dist_gemm_plan_s* P) {
+  std::vector<LaunchGroup> v;
+  for (int i = 0; i < static_cast<int>(P->steps.size()); ++i) {
+    const dist_gemm_step& s = P->steps[i];
+    if (!v.empty() && P->pr.schedule != DIST_GEMM_MONOLITHIC) {
+      LaunchGroup& b = v.back();
+      const dist_gemm_step& prev = P->steps[b.first + b.count - 1];
+      const bool adjacent = s.staged && prev.staged && s.slot == prev.slot + 1 &&
+                            s.shard == prev.shard + 1;
+      if (adjacent && b.count < P->max_group) {
+        ++b.count;
+        continue;
+      }
+    }
+    v.push_back({i, 1});
+  }
+  return v;
 }
 
 // GEMM parameters of one step.
@@ -262,7 +323,8 @@ dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, 
   const uint8_t* c = static_cast<const uint8_t*>(C);
   uint8_t* d = static_cast<uint8_t*>(D);
   const uint8_t* slot =
-      st.staged ? P->staging + static_cast<size_t>(st.slot) * P->slot_stride : nullptr;
+      st.staged ? P->staging + static_cast<size_t>(st.slot) * P->geom.width : nullptr;
+  const int64_t slots = S - 1;
 
   dg::GemmParams g{};
   g.K = static_cast<int32_t>(K);
@@ -278,14 +340,29 @@ dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, 
   g.D = d + (st.m0 * N + st.n0) * eo; g.ldd = N; g.sD = M * N;
   if (st.staged) {
     switch (pr.schedule) {
-      case DIST_GEMM_AG_ROT_A: g.A = slot; g.sA = (M / S) * K; break;
-      case DIST_GEMM_AG_ROT_B: g.B = slot; g.sB = (N / S) * K; break;
-      case DIST_GEMM_RS_TILE_A_ROT_C: g.C = slot; g.ldc = N; g.sC = (M / S) * N; break;
-      case DIST_GEMM_RS_TILE_B_ROT_C: g.C = slot; g.ldc = N / S; g.sC = M * (N / S); break;
+      case DIST_GEMM_AG_ROT_A: g.A = slot; g.sA = slots * (M / S) * K; break;
+      case DIST_GEMM_AG_ROT_B: g.B = slot; g.sB = slots * (N / S) * K; break;
+      case DIST_GEMM_RS_TILE_A_ROT_C: g.C = slot; g.ldc = N; g.sC = slots * (M / S) * N; break;
+      case DIST_GEMM_RS_TILE_B_ROT_C:
+        g.C = slot; g.ldc = slots * (N / S); g.sC = M * slots * (N / S); break;
       default: break;
     }
   }
   if (beta == 0.0f) g.C = nullptr;
+  return g;
+}
+
+// GEMM parameters of a launch group: the first step's operands, extended
+// over the group's rows (row schedules) or columns.  The group's shards are
+// adjacent in the source operand, in the staging buffer and in D, so the
+// extended views address exactly the member steps' data.
+dg::GemmParams group_params(const dist_gemm_plan_s* P, const LaunchGroup& grp, const void* A,
+                            const void* B, const void* C, void* D, float alpha, float beta) {
+  const dist_gemm_step& f = P->steps[grp.first];
+  const dist_gemm_step& l = P->steps[grp.first + grp.count - 1];
+  dg::GemmParams g = step_params(P, f, A, B, C, D, alpha, beta);
+  g.M = static_cast<int32_t>(std::max(f.m1, l.m1) - f.m0);
+  g.N = static_cast<int32_t>(std::max(f.n1, l.n1) - f.n0);
   return g;
 }
 
@@ -349,20 +426,18 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
   std::string* perr = nullptr;  // errors before the handle is returned go to the thread slot
   const int n_slots = pr.S - 1;
   if (pr.schedule != DIST_GEMM_MONOLITHIC && n_slots > 0) {
-    P->slot_stride = (P->geom.slot_bytes() + 255) & ~static_cast<size_t>(255);
-    e = hipMalloc(&P->staging, P->slot_stride * n_slots);
+    P->staging_pitch = P->geom.staging_pitch(n_slots);
+    e = hipMalloc(&P->staging, P->staging_pitch * P->geom.height);
     if (e != hipSuccess) {
       release(P);
       (void)hipGetLastError();
       return fail(perr, DIST_GEMM_ERR_OOM, "staging allocation of " +
-                                               std::to_string(P->slot_stride * n_slots) + " bytes");
+                                               std::to_string(P->staging_pitch * P->geom.height) + " bytes");
     }
   }
   auto mk = [&](hipEvent_t* ev, unsigned flags) { return hipEventCreateWithFlags(ev, flags); };
-  e = hipStreamCreateWithFlags(&P->side, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&P->cs2, hipStreamNonBlocking);
+  e = hipStreamCreateWithFlags(&P->cs2, hipStreamNonBlocking);
   if (e == hipSuccess) e = mk(&P->ev_start, hipEventDisableTiming);
-  if (e == hipSuccess) e = mk(&P->ev_side_done, hipEventDisableTiming);
   if (e == hipSuccess) e = mk(&P->ev_cs2_done, hipEventDisableTiming);
   if (e == hipSuccess) e = mk(&P->ev_done, hipEventDisableTiming);
   P->ev_copy.assign(pr.S, nullptr);
@@ -370,6 +445,11 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
   if (e != hipSuccess) {
     release(P);
     return hip_fail(perr, e, "stream/event creation");
+  }
+  rc = ensure_sides(P, std::min(P->copy_streams, std::max(pr.S - 1, 1)), perr);
+  if (rc != DIST_GEMM_OK) {
+    release(P);
+    return rc;
   }
   *out = P;
   return DIST_GEMM_OK;
@@ -397,6 +477,21 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy engine must be 0 or 1");
       plan->copy_engine = static_cast<int>(value);
       return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_COPY_STREAMS: {
+      if (value < 1 || value > 8)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy streams must be 1..8");
+      DeviceGuard guard(plan->device);
+      const int rc = ensure_sides(plan, std::min<int>(static_cast<int>(value),
+                                                      std::max(plan->pr.S - 1, 1)), &plan->err);
+      if (rc != DIST_GEMM_OK) return rc;
+      plan->copy_streams = static_cast<int>(value);
+      return DIST_GEMM_OK;
+    }
+    case DIST_GEMM_OPT_STEP_GROUP:
+      if (value < 1 || value > 1024)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "step group must be 1..1024");
+      plan->max_group = static_cast<int>(value);
+      return DIST_GEMM_OK;
     case DIST_GEMM_OPT_STEP_TIMING: {
       if (value < 0 || value > 4096)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "step timing keeps 0..4096 runs");
@@ -404,16 +499,29 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       if (plan->ev_done && plan->has_prev) (void)hipEventSynchronize(plan->ev_done);
       for (hipEvent_t ev : plan->t_begin) if (ev) (void)hipEventDestroy(ev);
       for (hipEvent_t ev : plan->t_end) if (ev) (void)hipEventDestroy(ev);
+      for (hipEvent_t ev : plan->t_run0) if (ev) (void)hipEventDestroy(ev);
+      for (hipEvent_t ev : plan->t_copy) if (ev) (void)hipEventDestroy(ev);
+      plan->t_first.clear();
       plan->t_begin.clear();
       plan->t_end.clear();
+      plan->t_run0.clear();
+      plan->t_copy.clear();
       plan->step_timing = 0;
       plan->timed_runs = 0;
       const size_t n = static_cast<size_t>(value) * plan->steps.size();
       plan->t_begin.assign(n, nullptr);
       plan->t_end.assign(n, nullptr);
+      plan->t_copy.assign(n, nullptr);
+      plan->t_first.assign(n, 0);
+      plan->t_run0.assign(static_cast<size_t>(value), nullptr);
       for (size_t i = 0; i < n; ++i) {
         hipError_t e = hipEventCreate(&plan->t_begin[i]);
         if (e == hipSuccess) e = hipEventCreate(&plan->t_end[i]);
+        if (e == hipSuccess) e = hipEventCreate(&plan->t_copy[i]);
+        if (e != hipSuccess) return hip_fail(&plan->err, e, "timing event creation");
+      }
+      for (hipEvent_t& ev : plan->t_run0) {
+        const hipError_t e = hipEventCreate(&ev);
         if (e != hipSuccess) return hip_fail(&plan->err, e, "timing event creation");
       }
       plan->step_timing = static_cast<int>(value);
@@ -452,35 +560,49 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
                 "the reduce-scatter schedules rotate C: C must be non-NULL");
   }
 
+  // side streams in use: the first n, n = min(copy streams, staged copies)
+  const int n_side = rotating ? std::min(P->copy_streams, pr.S - 1) : 0;
+  if (n_side > static_cast<int>(P->sides.size()))
+    return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "copy streams not created");
+
   if (P->has_prev && P->prev_stream != st) DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_done, 0));
   DG_HIP(&P->err, hipEventRecord(P->ev_start, st));
-  if (rotating) DG_HIP(&P->err, hipStreamWaitEvent(P->side, P->ev_start, 0));
+  const size_t trun = P->step_timing ? static_cast<size_t>(P->timed_runs % P->step_timing) : 0;
+  const size_t tbase = trun * P->steps.size();
+  if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_run0[trun], st));
+  for (int k = 0; k < n_side; ++k) DG_HIP(&P->err, hipStreamWaitEvent(P->sides[k], P->ev_start, 0));
   if (two) DG_HIP(&P->err, hipStreamWaitEvent(P->cs2, P->ev_start, 0));
 
-  // Copy engine: every staged operand, in step order, one event per copy.
+  // Copy engine: every staged operand, in step order, round-robin over the
+  // side streams, one event per copy.
   if (rotating) {
     for (const dist_gemm_step& s : P->steps) {
       if (!s.staged) continue;
-      int rc = enqueue_copy(P, copy_src, s.shard, s.slot);
+      hipStream_t side = P->sides[s.slot % n_side];
+      int rc = enqueue_copy(P, side, copy_src, s.shard, s.slot);
       if (rc != DIST_GEMM_OK) return rc;
-      DG_HIP(&P->err, hipEventRecord(P->ev_copy[s.step], P->side));
+      DG_HIP(&P->err, hipEventRecord(P->ev_copy[s.step], side));
+      if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_copy[tbase + s.step], side));
     }
   }
-  // Step GEMMs.
-  const size_t tbase =
-      P->step_timing ? static_cast<size_t>(P->timed_runs % P->step_timing) * P->steps.size() : 0;
-  for (const dist_gemm_step& s : P->steps) {
-    hipStream_t cs = (two && (s.step & 1)) ? P->cs2 : st;
-    if (s.staged) DG_HIP(&P->err, hipStreamWaitEvent(cs, P->ev_copy[s.step], 0));
-    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_begin[tbase + s.step], cs));
-    const dg::GemmParams g = step_params(P, s, A, B, C, D, alpha_eff, beta);
+  // Step GEMMs: one launch per group, alternating compute streams by launch.
+  const std::vector<LaunchGroup> groups = group_steps(P);
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const LaunchGroup& grp = groups[gi];
+    hipStream_t cs = (two && (gi & 1)) ? P->cs2 : st;
+    for (int k = grp.first; k < grp.first + grp.count; ++k) {
+      if (P->steps[k].staged) DG_HIP(&P->err, hipStreamWaitEvent(cs, P->ev_copy[k], 0));
+      if (P->step_timing) P->t_first[tbase + k] = grp.first;
+    }
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_begin[tbase + grp.first], cs));
+    const dg::GemmParams g = group_params(P, grp, A, B, C, D, alpha_eff, beta);
     DG_HIP(&P->err, dg::launch_gemm(pr.in_kind, pr.out_kind, g, cs));
-    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[tbase + s.step], cs));
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[tbase + grp.first], cs));
   }
   // Join the side streams back into the caller's stream.
-  if (rotating) {
-    DG_HIP(&P->err, hipEventRecord(P->ev_side_done, P->side));
-    DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_side_done, 0));
+  for (int k = 0; k < n_side; ++k) {
+    DG_HIP(&P->err, hipEventRecord(P->ev_side_done[k], P->sides[k]));
+    DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_side_done[k], 0));
   }
   if (two) {
     DG_HIP(&P->err, hipEventRecord(P->ev_cs2_done, P->cs2));
@@ -515,12 +637,43 @@ int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n) {
   int64_t w = 0;
   for (int64_t r = plan->timed_runs - R; r < plan->timed_runs; ++r) {
     const size_t base = static_cast<size_t>(r % plan->step_timing) * S;
-    for (int64_t s = 0; s < S; ++s, ++w)
-      if (w < cap)
-        DG_HIP(&plan->err,
-               hipEventElapsedTime(&ms[w], plan->t_begin[base + s], plan->t_end[base + s]));
+    for (int64_t s = 0; s < S; ++s, ++w) {
+      if (w >= cap) continue;
+      const int f = plan->t_first[base + s];
+      int members = 0;
+      for (int64_t k = 0; k < S; ++k) members += plan->t_first[base + k] == f;
+      float t = 0.0f;
+      DG_HIP(&plan->err, hipEventElapsedTime(&t, plan->t_begin[base + f], plan->t_end[base + f]));
+      ms[w] = t / static_cast<float>(members);
+    }
   }
   *n = static_cast<int>(R * S);
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n) {
+  if (!plan || !n) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan or n is NULL");
+  if (!plan->step_timing || plan->timed_runs == 0)
+    return fail(&plan->err, DIST_GEMM_ERR_UNSUPPORTED, "no timed run recorded");
+  DeviceGuard guard(plan->device);
+  const int64_t S = static_cast<int64_t>(plan->steps.size());
+  const int64_t cap = *n;
+  if (cap > 0 && !ms) return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "ms is NULL");
+  DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+  const size_t run = static_cast<size_t>((plan->timed_runs - 1) % plan->step_timing);
+  const size_t base = run * static_cast<size_t>(S);
+  hipEvent_t t0 = plan->t_run0[run];
+  for (int64_t s = 0; s < S; ++s) {
+    float v[3] = {-1.0f, 0.0f, 0.0f};
+    const bool staged = plan->steps[s].staged && plan->pr.schedule != DIST_GEMM_MONOLITHIC;
+    if (staged) DG_HIP(&plan->err, hipEventElapsedTime(&v[0], t0, plan->t_copy[base + s]));
+    const int f = plan->t_first[base + s];
+    DG_HIP(&plan->err, hipEventElapsedTime(&v[1], t0, plan->t_begin[base + f]));
+    DG_HIP(&plan->err, hipEventElapsedTime(&v[2], t0, plan->t_end[base + f]));
+    for (int k = 0; k < 3; ++k)
+      if (3 * s + k < cap) ms[3 * s + k] = v[k];
+  }
+  *n = static_cast<int>(3 * S);
   return DIST_GEMM_OK;
 }
 

@@ -127,6 +127,8 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
 int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
 
 /* Tuning options (host state of the plan; take effect at the next run).
+ * Returns INVALID_ARG for a NULL plan, an unknown option or a value out of
+ * range; the plan is unchanged then.
  *   DIST_GEMM_OPT_COMPUTE_STREAMS: 1 = all step GEMMs on the caller's
  *     stream; 2 (default) = steps alternate between the caller's stream and
  *     the plan's second compute stream by step parity, so the tail of one
@@ -137,11 +139,28 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
  *   DIST_GEMM_OPT_STEP_TIMING: V > 0 = record a HIP event pair around every
  *     step GEMM on the stream it is launched on, keeping the pairs of the
  *     last V runs (V <= 4096); read with dist_gemm_step_times.  0 (default)
- *     = off.  Setting it waits for the plan's last run and clears the record. */
+ *     = off.  Setting it waits for the plan's last run and clears the record.
+ *   DIST_GEMM_OPT_COPY_STREAMS: n in 1..8 side streams carry the shard
+ *     copies; staged copy k (k = 0 .. S-2, in step order) goes to side
+ *     stream k mod n.  An all-gather pulls step s's shard from peer
+ *     (r+s) mod S, so on a fully connected xGMI node every step's transfer
+ *     has a link of its own and the transfers of different steps run
+ *     concurrently; n copy streams stand in for n such links.  Default 2
+ *     (with the two compute streams, four streams: the hardware queues a
+ *     process gets by default).
+ *   DIST_GEMM_OPT_STEP_GROUP: g in 1..1024 = at most g consecutive staged
+ *     steps run as one GEMM launch once all of their shards have arrived.
+ *     Consecutive steps consume adjacent shards (rows of A, columns of B or
+ *     of the partial) that sit in adjacent staging slots, so their GEMMs
+ *     are one GEMM over the union; every output element is computed exactly
+ *     as by its own step.  The step that uses the local shard launches
+ *     alone.  1 = one launch per step; default 2. */
 enum dist_gemm_option {
   DIST_GEMM_OPT_COMPUTE_STREAMS = 0,
   DIST_GEMM_OPT_COPY_ENGINE = 1,
-  DIST_GEMM_OPT_STEP_TIMING = 2
+  DIST_GEMM_OPT_STEP_TIMING = 2,
+  DIST_GEMM_OPT_COPY_STREAMS = 3,
+  DIST_GEMM_OPT_STEP_GROUP = 4
 };
 int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
 
@@ -165,8 +184,17 @@ int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_step
 /* With DIST_GEMM_OPT_STEP_TIMING = V set: wait for the last run to finish and
  * write the step GEMM durations in milliseconds of the last R = min(runs, V)
  * timed runs, oldest run first, steps in order (R * steps values, at most *n
- * written); *n receives R * steps.  UNSUPPORTED if no timed run exists. */
+ * written); *n receives R * steps.  Steps that ran as one launch share its
+ * duration equally.  UNSUPPORTED if no timed run exists. */
 int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n);
+
+/* With DIST_GEMM_OPT_STEP_TIMING set: wait for the last run to finish and
+ * write its timeline, three values per step in step order, in milliseconds
+ * since the run was enqueued on its stream: [3s] = the moment the step's
+ * shard copy completed (-1 for a step that consumes no copy), [3s+1] = the
+ * GEMM launch that computed it began, [3s+2] = it ended.  At most *n values are written; *n
+ * receives 3 * steps.  UNSUPPORTED if no timed run exists. */
+int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n);
 
 /* Synchronise the plan's streams, free its staging, streams and events, and
  * the handle.  NULL is accepted (no-op). */

@@ -14,8 +14,12 @@ def pytest_configure(config):
     pkg = os.path.join(ROOT, "communication_tensor_gemm_amd")
     lib = os.path.join(pkg, "libdistgemm.so")
     if os.path.isdir(pkg) and not os.path.exists(lib):
-        from communication_tensor_gemm_amd.build import build
-        build()
+        # by path: importing the package needs the library that is missing
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("_distgemm_build", os.path.join(pkg, "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 def pytest_collection_modifyitems(config, items):

@@ -67,6 +67,26 @@ def test_edge_shapes(M, N, K, TP, sched, dtype):
     check_full(w, x, D)
 
 
+@pytest.mark.parametrize("group", [2, 3, 8])
+@pytest.mark.parametrize("dtype", ["F32", "BF16_BF16", "E4M3_F32"])
+@pytest.mark.parametrize("sched", ["AG_ROT_A", "AG_ROT_B", "RS_TILE_A_ROT_C", "RS_TILE_B_ROT_C"])
+def test_step_groups(sched, dtype, group):
+    # TP=8 on 600 x 520: 75-row / 65-column shards, so merged launches have
+    # tiles that straddle shard boundaries; L=2 exercises the batch strides
+    # of the side-by-side staging layout.
+    import torch
+    beta = 1.0 if sched.startswith("RS") else 0.5
+    w = workloads.small_case(f"group_{sched}_{dtype}_{group}", sched, dtype, 600, 520, 96, 2, 8,
+                             1.5, beta, seed=group * 7 + len(sched))
+    x = workloads.generate(w)
+    log("case", w.name, "STEP_GROUP", group)
+    dev = (to_gpu(x.A), to_gpu(x.B), to_gpu(x.C))
+    Dg = run_plan(w, x, dev=dev, options={"STEP_GROUP": group})
+    check_full(w, x, Dg)
+    D1 = run_plan(w, x, dev=dev, options={"STEP_GROUP": 1})
+    assert torch.equal(Dg, D1), "grouped launches differ from one launch per step"
+
+
 def test_alpha_zero_and_beta_zero_ignores_c():
     import torch
     w = workloads.small_case("a0", "AG_ROT_A", "BF16_F32", 512, 256, 64, 1, 2, 0.0, 0.75, seed=3)
@@ -109,6 +129,12 @@ def test_run_errors():
             dg.dist_gemm_run(p.handle, A, A, D, D, float("nan"), 1.0)
         with pytest.raises(dg.DistGemmError):
             dg.dist_gemm_set_option(p.handle, "COMPUTE_STREAMS", 3)
+        for bad in (0, 9):
+            with pytest.raises(dg.DistGemmError):
+                dg.dist_gemm_set_option(p.handle, "COPY_STREAMS", bad)
+        for bad in (0, 1025):
+            with pytest.raises(dg.DistGemmError):
+                dg.dist_gemm_set_option(p.handle, "STEP_GROUP", bad)
         with pytest.raises(ValueError):
             p.run(A[:10], A, D, D, 1.0, 1.0)               # too small for 64 x 64
     with pytest.raises(dg.DistGemmError) as ei:

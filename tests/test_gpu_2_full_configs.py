@@ -45,6 +45,14 @@ def test_full_config(name):
     Db = run_plan(w, x, dev=dev, options={"COPY_ENGINE": 1})
     assert torch.equal(D, Db), "SDMA copies != default copies"
     del Db
+    for n in (1, 7):
+        Dn = run_plan(w, x, dev=dev, options={"COPY_STREAMS": n})
+        assert torch.equal(D, Dn), f"{n} copy streams != the default"
+        del Dn
+    for g in (1, 2, 7):
+        Dg = run_plan(w, x, dev=dev, options={"STEP_GROUP": g})
+        assert torch.equal(D, Dg), f"step groups of {g} != the default"
+        del Dg
     if w.out_dtype == "f32":
         assert torch.isfinite(D).all()
     torch.cuda.synchronize()
