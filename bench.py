@@ -64,14 +64,21 @@ def timed_runs(plan, args_run, steps, warmup, timing_runs):
     torch.cuda.synchronize()
     if timing_runs:
         plan.set_option("STEP_TIMING", steps)
+    # per-run events on the stream the runs are enqueued on (the null stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for b, e in evs:
+        b.record()
         plan.run(*args_run)
+        e.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms = plan.step_times() if timing_runs else []
-    return (t1 - t0) / steps * 1e3, step_ms
+    run_ms = sorted(b.elapsed_time(e) for b, e in evs)
+    stats = {"mean": sum(run_ms) / len(run_ms), "median": run_ms[len(run_ms) // 2], "min": run_ms[0]}
+    return (t1 - t0) / steps * 1e3, step_ms, stats
 
 
 def cpu_baseline(w, x, rows_per_block):
@@ -226,7 +233,7 @@ def main():
     plan.set_option("STEP_GROUP", args.step_group)
     run_args = (A, B, C if w.beta != 0 else None, D, w.alpha, w.beta)
     log(f"[bench] timing {args.steps} runs after {args.warmup} warmup runs")
-    ms, step_ms = timed_runs(plan, run_args, args.steps, args.warmup, True)
+    ms, step_ms, run_stats = timed_runs(plan, run_args, args.steps, args.warmup, True)
     value = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK[w.in_dtype]
     # Steps merged into one launch share its duration equally, so the mean
@@ -264,9 +271,10 @@ def main():
         with dg.Plan(w.M, w.N, w.K, w.L, 1, "MONOLITHIC", w.dtype) as mp:
             if w.in_dtype == "e4m3":
                 mp.set_scales(x.scale_a, x.scale_b)
-            mono_ms, mono_steps = timed_runs(mp, run_args, args.steps, args.warmup, True)
+            mono_ms, mono_steps, mono_stats = timed_runs(mp, run_args, args.steps, args.warmup, True)
         mono = {"ms": mono_ms, "tflops": w.flops / (mono_ms * 1e-3) / 1e12,
                 "kernel_ms": float(np.mean(mono_steps)),
+                "run_ms": {k: round(v, 4) for k, v in mono_stats.items()},
                 "exposed_overhead": ms / mono_ms - 1.0}
         log(f"[bench] monolithic {mono_ms:.3f} ms ({mono['tflops']:.1f} TFLOP/s); "
             f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
@@ -311,6 +319,7 @@ def main():
         "timeline_last_run": {"copy_done_ms": [round(t[0], 4) for t in timeline],
                               "gemm_begin_ms": [round(t[1], 4) for t in timeline],
                               "gemm_end_ms": [round(t[2], 4) for t in timeline]},
+        "run_ms": {k: round(v, 4) for k, v in run_stats.items()},
         "monolithic": mono,
         "parity": parity,
         "cpu_baseline": cpu,
