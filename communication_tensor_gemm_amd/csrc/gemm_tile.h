@@ -170,10 +170,10 @@ struct Mma16Base {
   typedef i32x4 Frags[16];  // 0..7: A blocks, 8..15: B blocks
   // reads r and r+1 are 16 rows (two 8-row LDS blocks) apart
   static constexpr int kReadStride = 2 * 1024;
-  __device__ static int base_row(int lane, int odd) { return lane & 15; }
-  __device__ static int base_chunk(int lane, int odd) { return lane >> 4; }
+  __device__ __forceinline__ static int base_row(int lane, int odd) { return lane & 15; }
+  __device__ __forceinline__ static int base_chunk(int lane, int odd) { return lane >> 4; }
   // read q: A block q/2 (q even) or B block q/2 (q odd)
-  __device__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+  __device__ __forceinline__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
                               Frags& F) {
     const int r = q >> 1;
     if ((q & 1) == 0)
@@ -182,8 +182,8 @@ struct Mma16Base {
       F[8 + r] = *reinterpret_cast<const i32x4*>(b + fb[2] + kReadStride * r);
   }
   // MFMA 16 x 16 result: lane holds column lane%16, rows 4*(lane/16) + r
-  __device__ static int out_row(int i, int r, int lane) { return 16 * i + 4 * (lane >> 4) + r; }
-  __device__ static int out_col(int j, int lane) { return 16 * j + (lane & 15); }
+  __device__ __forceinline__ static int out_row(int i, int r, int lane) { return 16 * i + 4 * (lane >> 4) + r; }
+  __device__ __forceinline__ static int out_col(int j, int lane) { return 16 * j + (lane & 15); }
 };
 
 template <>
@@ -192,7 +192,7 @@ struct Mma<IN_BF16> : Mma16Base {
   static constexpr int kReadAt = 1, kReadEvery = 2, kReadsPer = 1;
   static constexpr int kDmaAt = 2, kDmaEvery = 8;
   // MFMA m: block (m / 8, m % 8)
-  __device__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
+  __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
     const int i = m >> 3, j = m & 7;
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
                  : "+a"(acc[i][j])
@@ -208,7 +208,7 @@ struct Mma<IN_F32> : Mma16Base {
   // MFMA m: K step t = m / 64 of block ((m / 8) % 8, m % 8).  The lane's 4
   // floats of a block are K values 4*(lane/16) + t; the 16x16x4 MFMA takes
   // lane group lane/16 as its K index, identically for A and B.
-  __device__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
+  __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
     const int t = m >> 6, i = (m >> 3) & 7, j = m & 7;
     const float a = __builtin_bit_cast(f32x4, F[i])[t];
     const float b = __builtin_bit_cast(f32x4, F[8 + j])[t];
@@ -226,10 +226,10 @@ struct Mma32Base {
   typedef i32x8 Frags[8];  // 0..3: A blocks, 4..7: B blocks (32 bytes per lane)
   // block b is 32 rows (four 8-row LDS blocks) further on
   static constexpr int kReadStride = 4 * 1024;
-  __device__ static int base_row(int lane, int odd) { return lane & 31; }
-  __device__ static int base_chunk(int lane, int odd) { return 2 * (lane >> 5) + odd; }
+  __device__ __forceinline__ static int base_row(int lane, int odd) { return lane & 31; }
+  __device__ __forceinline__ static int base_chunk(int lane, int odd) { return 2 * (lane >> 5) + odd; }
   // read q: block q/4 of A (q%4 < 2) or B, half q%2 of its 32 bytes
-  __device__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+  __device__ __forceinline__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
                               Frags& F) {
     const int blk = q >> 2, op = (q >> 1) & 1, h = q & 1;
     const i32x4 v = *reinterpret_cast<const i32x4*>((op ? b : a) + fb[2 * op + h] +
@@ -240,10 +240,10 @@ struct Mma32Base {
       F[4 * op + blk].hi = v;
   }
   // MFMA 32 x 32 result: lane holds column lane%32, rows 8*(r/4) + 4*(lane/32) + r%4
-  __device__ static int out_row(int i, int r, int lane) {
+  __device__ __forceinline__ static int out_row(int i, int r, int lane) {
     return 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
   }
-  __device__ static int out_col(int j, int lane) { return 32 * j + (lane & 31); }
+  __device__ __forceinline__ static int out_col(int j, int lane) { return 32 * j + (lane & 31); }
 };
 
 template <>
@@ -252,7 +252,7 @@ struct Mma<IN_E4M3> : Mma32Base {
   static constexpr int kReadAt = 0, kReadEvery = 1, kReadsPer = 2;
   static constexpr int kDmaAt = 0, kDmaEvery = 1;
   // MFMA m: block (m / 4, m % 4); format fields 0/0 select e4m3 for A and B
-  __device__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
+  __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
     const int i = m >> 2, j = m & 3;
     asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
                  : "+a"(acc[i][j])
@@ -343,6 +343,96 @@ __device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int k
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Element-by-element epilogue of a wave's 128 x 128 block (any alignment).
+template <typename M, int OUT>
+__device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc (&acc)[M::NB][M::NB],
+                                                const GemmParams& p, uint8_t* Dw, const uint8_t* Cw,
+                                                int rows_left, int cols_left) {
+  constexpr int OES = OUT == OUT_F32 ? 4 : 2;
+#pragma unroll
+  for (int i = 0; i < M::NB; ++i) {
+#pragma unroll
+    for (int r = 0; r < M::R; ++r) {
+      const int row = M::out_row(i, r, lane);
+      if (row >= rows_left) continue;
+      uint8_t* drow = Dw + static_cast<int64_t>(row) * p.ldd * OES;
+      const uint8_t* crow = Cw ? Cw + static_cast<int64_t>(row) * p.ldc * OES : nullptr;
+#pragma unroll
+      for (int j = 0; j < M::NB; ++j) {
+        const int col = M::out_col(j, lane);
+        if (col < cols_left) {
+          float v = p.alpha * acc[i][j][r];
+          if (crow) v = __builtin_fmaf(p.beta, load_out<OUT>(crow, col), v);
+          store_out<OUT>(drow, col, v);
+        }
+      }
+    }
+  }
+}
+
+// LDS-staged epilogue (fp32 output): each 32-row quarter of the wave's block
+// is written to the wave's 32 x 132-float LDS area in the MFMA layout and read
+// back by rows, 4 consecutive values per lane (one 16-byte LDS read), so a
+// lane stores 16 contiguous bytes with one instruction.  Measured: +10% on a
+// 2048 x 13312 x 16384 bf16 GEMM, +2% on e4m3 with fp32 output.  For bf16
+// output the element-wise stores are kept: the staged form measured equal for
+// bf16 inputs and 17% slower for e4m3 inputs.  The LDS ring is free by now; the
+// barrier makes sure no wave still reads it.
+constexpr int kEpiRow = 128 + 4;             // floats per staged row (padded)
+constexpr int kEpiWave = 32 * kEpiRow;       // floats per wave: 16.5 KiB
+
+template <typename M>
+__device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lane,
+                                                const typename M::Acc (&acc)[M::NB][M::NB],
+                                                const GemmParams& p, uint8_t* Dw, const uint8_t* Cw,
+                                                int rows_left, int cols_left) {
+  barrier_only();
+  float* lds = reinterpret_cast<float*>(smem) + wave * kEpiWave;
+  constexpr int kBlocksPerQuarter = 32 / M::BLK;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int ib = 0; ib < kBlocksPerQuarter; ++ib) {
+      const int i = q * kBlocksPerQuarter + ib;
+#pragma unroll
+      for (int r = 0; r < M::R; ++r)
+#pragma unroll
+        for (int j = 0; j < M::NB; ++j)
+          lds[(M::out_row(i, r, lane) - 32 * q) * kEpiRow + M::out_col(j, lane)] = acc[i][j][r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    {
+      // 32 lanes per row, 4 floats each; two rows per instruction
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int rr = 2 * t + (lane >> 5), cc = 4 * (lane & 31), row = 32 * q + rr;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&lds[rr * kEpiRow + cc]);
+        if (row >= rows_left) continue;
+        float* drow = reinterpret_cast<float*>(Dw) + static_cast<int64_t>(row) * p.ldd;
+        const float* crow = Cw ? reinterpret_cast<const float*>(Cw) + static_cast<int64_t>(row) * p.ldc : nullptr;
+        if (cc + 4 <= cols_left) {
+          f32x4 v = a * p.alpha;
+          if (crow) {
+            const f32x4 c = *reinterpret_cast<const f32x4*>(crow + cc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, c[e], v[e]);
+          }
+          *reinterpret_cast<f32x4*>(drow + cc) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (cc + e < cols_left) {
+              float v = p.alpha * a[e];
+              if (crow) v = __builtin_fmaf(p.beta, crow[cc + e], v);
+              drow[cc + e] = v;
+            }
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
   }
 }
 
@@ -463,39 +553,43 @@ gemm_tn_kernel(GemmParams p) {
   wait_lgkmcnt0();
   half_step<IN, false, false, 1>(c, smem, kt, s, smem, smem, fb, F1, F0, acc);
   // The MFMAs are opaque to the compiler's hazard tracking: give the last
-  // ones their result latency before the epilogue reads the AGPRs.
+  // ones their result latency, then redefine every accumulator after that
+  // wait, so that no AGPR read of the epilogue can be scheduled above it (a
+  // read of a block finished early in the last half slab otherwise may be,
+  // and returns the value without that half slab).
   asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < M::NB; ++i)
+#pragma unroll
+    for (int j = 0; j < M::NB; ++j) asm volatile("" : "+a"(acc[i][j]));
 
-  // Epilogue: D = alpha * acc + beta * C, through a per-wave base pointer.
+  // Epilogue: D = alpha * acc + beta * C.  For fp32 output with D (and C)
+  // rows 16-byte aligned, each 32-row quarter of the wave's block goes through
+  // LDS so that every lane stores 16 contiguous bytes; otherwise element by
+  // element.
+  constexpr int OES = OUT == OUT_F32 ? 4 : 2;
+  const bool use_c = p.beta != 0.0f;
+  const uint8_t* Dl = static_cast<const uint8_t*>(p.D) + l * p.sD * OES;
+  const uint8_t* Cl = use_c ? static_cast<const uint8_t*>(p.C) + l * p.sC * OES : nullptr;
+  [[maybe_unused]] const uint64_t align = reinterpret_cast<uint64_t>(Dl) | static_cast<uint64_t>(p.ldd * OES) |
+                         (use_c ? reinterpret_cast<uint64_t>(Cl) | static_cast<uint64_t>(p.ldc * OES) : 0);
   const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
   const int rows_left = p.M - wrow0, cols_left = p.N - wcol0;
-  constexpr int OES = OUT == OUT_F32 ? 4 : 2;
-  uint8_t* Dw = static_cast<uint8_t*>(p.D) + (l * p.sD + static_cast<int64_t>(wrow0) * p.ldd +
-                                               wcol0) * OES;
-  const uint8_t* Cw =
-      p.beta != 0.0f ? static_cast<const uint8_t*>(p.C) +
-                           (l * p.sC + static_cast<int64_t>(wrow0) * p.ldc + wcol0) * OES
-                     : nullptr;
-  const bool use_c = p.beta != 0.0f;
-#pragma unroll
-  for (int i = 0; i < M::NB; ++i) {
-#pragma unroll
-    for (int r = 0; r < M::R; ++r) {
-      const int row = M::out_row(i, r, lane);
-      if (row >= rows_left) continue;
-      uint8_t* drow = Dw + static_cast<int64_t>(row) * p.ldd * OES;
-      const uint8_t* crow = use_c ? Cw + static_cast<int64_t>(row) * p.ldc * OES : nullptr;
-#pragma unroll
-      for (int j = 0; j < M::NB; ++j) {
-        const int col = M::out_col(j, lane);
-        if (col < cols_left) {
-          float v = p.alpha * acc[i][j][r];
-          if (use_c) v = __builtin_fmaf(p.beta, load_out<OUT>(crow, col), v);
-          store_out<OUT>(drow, col, v);
-        }
-      }
+  uint8_t* Dw = const_cast<uint8_t*>(Dl) + (static_cast<int64_t>(wrow0) * p.ldd + wcol0) * OES;
+  const uint8_t* Cw = use_c ? Cl + (static_cast<int64_t>(wrow0) * p.ldc + wcol0) * OES : nullptr;
+  // lane index redefined here, so that the epilogue's per-lane address
+  // arithmetic is not hoisted above the main loop (where it would hold VGPRs
+  // the fragment buffers need)
+  int elane = lane;
+  asm volatile("" : "+v"(elane));
+  // the condition is uniform over the workgroup (the barrier inside needs that)
+  if constexpr (OUT == OUT_F32) {
+    if ((align & 15) == 0) {
+      epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, rows_left, cols_left);
+      return;
     }
   }
+  epilogue_direct<M, OUT>(elane, acc, p, Dw, Cw, rows_left, cols_left);
 }
 
 template <int IN, int OUT>
