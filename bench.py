@@ -185,7 +185,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--compute-streams", type=int, default=2)
-    ap.add_argument("--copy-engine", type=int, default=0, help="0 SDMA, 1 runtime default")
+    ap.add_argument("--copy-engine", type=int, default=1, help="0 SDMA, 1 runtime device copy (default)")
     ap.add_argument("--copy-streams", type=int, default=2, help="side streams for the shard copies (1..8)")
     ap.add_argument("--step-group", type=int, default=2, help="consecutive staged steps per GEMM launch")
     ap.add_argument("--cpu-rows", type=int, default=2048,

@@ -3,16 +3,21 @@
 // and the C ABI declared in include/distgemm.h.
 //
 // Mechanism (Distributed GEMM pull-request page, description): the operand
-// that arrives from a peer at every step is moved by the copy engine, not by
-// compute units, and each step's GEMM starts only after its operand is in
-// place.  On one GPU the peer's shard is a region of the caller's operand;
-// the copy engine here is SDMA (hipMemcpyDeviceToDeviceNoCU) on side
-// streams, one copy per staged step, each followed by an event that the
-// step's GEMM launch waits on.  Copies go round-robin to up to eight side
-// streams, one per peer link that the transfer stands in for.  Step GEMMs alternate between the caller's
-// stream and a second compute stream by step parity (the stream alternation
-// of the PyTorch symmetric-memory page's all-gather consumer), so the last,
-// partly filled wave of one step's workgroups can overlap the next step.
+// that arrives from a peer at every step is moved while the GEMM of the
+// current step runs, and each step's GEMM starts only after its operand is
+// in place.  On one GPU the peer's shard is a region of the caller's
+// operand, moved by a device-to-device hipMemcpyAsync into a staging slot on
+// a side stream, one copy per staged step, each followed by an event that
+// the launch computing the step waits on.  Copies go round-robin to up to
+// eight side streams, one per peer link that the transfer stands in for.
+// The copy is the runtime's device copy by default (a copy kernel, which
+// runs between GEMM workgroups); the SDMA engine (NoCU) is an option --
+// measured, it slows several-fold while the GEMMs load memory.
+// Consecutive staged steps whose shards are adjacent may run as one GEMM
+// launch; launches alternate between the caller's stream and a second
+// compute stream (the stream alternation of the PyTorch symmetric-memory
+// page's all-gather consumer), so the last, partly filled wave of one
+// launch overlaps the next.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -186,7 +191,7 @@ struct dist_gemm_plan_s {
   std::vector<int> t_first;
   float scale_a = 1.0f, scale_b = 1.0f;
   int compute_streams = 2;
-  int copy_engine = 0;
+  int copy_engine = 1;  // runtime device copy
   int copy_streams = 2;
   int max_group = 2;  // consecutive staged steps per launch
   int step_timing = 0;
