@@ -178,7 +178,13 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  * Buffers must stay allocated until the work completes on `stream`.  A run
  * on another stream first waits for the plan's previous run.
  * Errors: INVALID_ARG (NULL plan/A/B/D, C NULL with beta != 0, non-finite
- * alpha/beta); HIP if an enqueue fails (earlier steps may be enqueued). */
+ * alpha/beta); HIP if an enqueue fails (earlier steps may be enqueued).
+ * Graph capture: with DIST_GEMM_OPT_STEP_TIMING = 0 and the plan's previous
+ * run (if any) on the same stream, a run enqueues only copies, kernel
+ * launches and event record / wait pairs that fork from and join back into
+ * `stream`, so it can be captured into a HIP graph.  The graph uses the
+ * plan's staging buffer: its replays must not overlap other runs of the
+ * plan, and the plan must outlive the graph. */
 int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
                   float alpha, float beta, void* stream);
 

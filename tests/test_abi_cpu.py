@@ -79,6 +79,8 @@ def test_null_handles_are_rejected_without_gpu():
     n = ctypes.c_int(0)
     assert dg.lib.dist_gemm_step_table(8, 8, 16, 1, 2, 0, 0, None, None) == -1
     assert dg.lib.dist_gemm_plan_steps(None, None, ctypes.byref(n)) == -1
+    assert dg.lib.dist_gemm_step_times(None, None, ctypes.byref(n)) == -1
+    assert dg.lib.dist_gemm_step_timeline(None, None, ctypes.byref(n)) == -1
 
 
 def test_single_hip_runtime_in_process():
