@@ -185,7 +185,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--compute-streams", type=int, default=2)
-    ap.add_argument("--copy-engine", type=int, default=1, help="0 SDMA, 1 runtime device copy (default)")
+    ap.add_argument("--copy-engine", type=int, default=2,
+                    help="0 SDMA, 1 runtime device copy, 2 library copy kernel (default)")
     ap.add_argument("--copy-streams", type=int, default=2, help="side streams for the shard copies (1..8)")
     ap.add_argument("--step-group", type=int, default=2, help="consecutive staged steps per GEMM launch")
     ap.add_argument("--cpu-rows", type=int, default=2048,
@@ -305,7 +306,7 @@ def main():
         "config": {"workload": w.name, "schedule": w.schedule, "M": w.M, "N": w.N, "K": w.K,
                    "L": w.L, "TP": w.TP, "in": w.in_dtype, "out": w.out_dtype,
                    "alpha": w.alpha, "beta": w.beta, "compute_streams": args.compute_streams,
-                   "copy_engine": "sdma" if args.copy_engine == 0 else "runtime_default",
+                   "copy_engine": ["sdma", "runtime_device_copy", "copy_kernel"][args.copy_engine],
                    "copy_streams": args.copy_streams, "step_group": args.step_group},
         "pct_mfma_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,

@@ -10,9 +10,10 @@
 // a side stream, one copy per staged step, each followed by an event that
 // the launch computing the step waits on.  Copies go round-robin to up to
 // eight side streams, one per peer link that the transfer stands in for.
-// The copy is the runtime's device copy by default (a copy kernel, which
-// runs between GEMM workgroups); the SDMA engine (NoCU) is an option --
-// measured, it slows several-fold while the GEMMs load memory.
+// The copy is the library's streaming copy kernel by default (it runs
+// between GEMM workgroups); the runtime's device copy and the SDMA engine
+// (NoCU) are options -- measured, SDMA slows several-fold while the GEMMs
+// load memory.
 // Consecutive staged steps whose shards are adjacent may run as one GEMM
 // launch; launches alternate between the caller's stream and a second
 // compute stream (the stream alternation of the PyTorch symmetric-memory
@@ -191,7 +192,7 @@ struct dist_gemm_plan_s {
   std::vector<int> t_first;
   float scale_a = 1.0f, scale_b = 1.0f;
   int compute_streams = 2;
-  int copy_engine = 1;  // runtime device copy
+  int copy_engine = 2;  // library streaming copy kernel
   int copy_streams = 2;
   int max_group = 2;  // consecutive staged steps per launch
   int step_timing = 0;
@@ -262,6 +263,49 @@ int ensure_sides(dist_gemm_plan_s* P, int n, std::string* err) {
   return DIST_GEMM_OK;
 }
 
+// Streaming 2-D copy for the shard rotation: `height` rows of `width` bytes,
+// source rows `spitch` apart, destination rows `dpitch` apart.  Rows spread
+// over gridDim.y, units of T (16, 4 or 1 bytes) of a row over gridDim.x x
+// 256 threads.  Non-temporal loads and stores keep the copied bytes from
+// evicting the operand lines the concurrently running GEMM reuses in L2.
+typedef __attribute__((ext_vector_type(4))) unsigned int copy_u32x4;
+
+template <typename T>
+__global__ __launch_bounds__(256) void shard_copy_kernel(uint8_t* __restrict__ dst, size_t dpitch,
+                                                       const uint8_t* __restrict__ src, size_t spitch,
+                                                       size_t width, size_t height) {
+  const size_t units = width / sizeof(T);
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t r = blockIdx.y; r < height; r += gridDim.y) {
+    const T* s = reinterpret_cast<const T*>(src + r * spitch);
+    T* d = reinterpret_cast<T*>(dst + r * dpitch);
+    for (size_t c = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < units; c += stride)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+  }
+}
+
+hipError_t launch_shard_copy(uint8_t* dst, size_t dpitch, const uint8_t* src, size_t spitch,
+                             size_t width, size_t height, hipStream_t stream) {
+  const uint64_t align = reinterpret_cast<uint64_t>(dst) | reinterpret_cast<uint64_t>(src) |
+                         dpitch | spitch | width;
+  const size_t unit = (align % 16 == 0) ? 16 : (align % 4 == 0) ? 4 : 1;
+  const size_t units = width / unit;
+  // about 2048 workgroups of 256 threads in all, at least one row per grid row
+  const size_t gx = std::max<size_t>(1, std::min<size_t>((units + 1023) / 1024, 2048));
+  const size_t gy = std::max<size_t>(1, std::min<size_t>(height, 2048 / gx));
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+  if (unit == 16)
+    hipLaunchKernelGGL(shard_copy_kernel<copy_u32x4>, grid, dim3(256), 0, stream, dst, dpitch, src,
+                       spitch, width, height);
+  else if (unit == 4)
+    hipLaunchKernelGGL(shard_copy_kernel<uint32_t>, grid, dim3(256), 0, stream, dst, dpitch, src,
+                       spitch, width, height);
+  else
+    hipLaunchKernelGGL(shard_copy_kernel<uint8_t>, grid, dim3(256), 0, stream, dst, dpitch, src,
+                       spitch, width, height);
+  return hipGetLastError();
+}
+
 int enqueue_copy(dist_gemm_plan_s* P, hipStream_t side, const void* src_base, int shard, int slot) {
   const CopyGeom& g = P->geom;
   const Problem& pr = P->pr;
@@ -279,9 +323,14 @@ int enqueue_copy(dist_gemm_plan_s* P, hipStream_t side, const void* src_base, in
       return DIST_GEMM_OK;
   }
   uint8_t* dst = P->staging + static_cast<size_t>(slot) * g.width;
+  hipError_t e;
+  if (P->copy_engine == 2) {
+    e = launch_shard_copy(dst, P->staging_pitch, src, g.src_pitch, g.width, g.height, side);
+    if (e != hipSuccess) return hip_fail(&P->err, e, "shard copy kernel");
+    return DIST_GEMM_OK;
+  }
   const hipMemcpyKind kind =
       P->copy_engine == 0 ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
-  hipError_t e;
   if (g.height == 1)
     e = hipMemcpyAsync(dst, src, g.width, kind, side);
   else
@@ -478,8 +527,8 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       plan->compute_streams = static_cast<int>(value);
       return DIST_GEMM_OK;
     case DIST_GEMM_OPT_COPY_ENGINE:
-      if (value != 0 && value != 1)
-        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy engine must be 0 or 1");
+      if (value < 0 || value > 2)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy engine must be 0, 1 or 2");
       plan->copy_engine = static_cast<int>(value);
       return DIST_GEMM_OK;
     case DIST_GEMM_OPT_COPY_STREAMS: {

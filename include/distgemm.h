@@ -135,11 +135,13 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
  *     step's launch overlaps the next step (the alternation the PyTorch
  *     symmetric-memory page uses for its all-gather consumer).
  *   DIST_GEMM_OPT_COPY_ENGINE: 0 = SDMA copy engine
- *     (hipMemcpyDeviceToDeviceNoCU); 1 (default) = the runtime's device copy
- *     (hipMemcpyDeviceToDevice, a copy kernel).  Measured on MI355X: SDMA
- *     copies run at about 1 TB/s alone but several times slower while the
- *     step GEMMs load memory, and then gate the launches that wait for them;
- *     the copy kernel finishes in the gaps between GEMM workgroups.
+ *     (hipMemcpyDeviceToDeviceNoCU); 1 = the runtime's device copy
+ *     (hipMemcpyDeviceToDevice, a copy kernel); 2 (default) = the library's
+ *     streaming copy kernel (16-byte non-temporal loads and stores).
+ *     Measured on MI355X: SDMA copies run at about 1 TB/s alone but several
+ *     times slower while the step GEMMs load memory, and then gate the
+ *     launches that wait for them; a copy kernel finishes in the gaps
+ *     between GEMM workgroups.
  *   DIST_GEMM_OPT_STEP_TIMING: V > 0 = record a HIP event pair around every
  *     step GEMM on the stream it is launched on, keeping the pairs of the
  *     last V runs (V <= 4096); read with dist_gemm_step_times.  0 (default)

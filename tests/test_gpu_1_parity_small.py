@@ -87,6 +87,24 @@ def test_step_groups(sched, dtype, group):
     assert torch.equal(Dg, D1), "grouped launches differ from one launch per step"
 
 
+@pytest.mark.parametrize("dtype", ["F32", "BF16_BF16", "E4M3_BF16"])
+@pytest.mark.parametrize("sched", ["AG_ROT_A", "AG_ROT_B", "RS_TILE_A_ROT_C", "RS_TILE_B_ROT_C"])
+def test_copy_engines_agree(sched, dtype):
+    # 600 x 518 at TP=2 with L=2: odd row and column widths, so the library
+    # copy kernel takes its 16-, 4- and 1-byte paths; every engine must give
+    # the same bits
+    import torch
+    beta = 1.0 if sched.startswith("RS") else 0.25
+    w = workloads.small_case(f"engines_{sched}_{dtype}", sched, dtype, 600, 518, 112, 2, 2, 1.0,
+                             beta, seed=5 + len(sched))
+    x = workloads.generate(w)
+    dev = (to_gpu(x.A), to_gpu(x.B), to_gpu(x.C))
+    log("case", w.name)
+    outs = [run_plan(w, x, dev=dev, options={"COPY_ENGINE": e}) for e in (0, 1, 2)]
+    check_full(w, x, outs[2])
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
 def test_alpha_zero_and_beta_zero_ignores_c():
     import torch
     w = workloads.small_case("a0", "AG_ROT_A", "BF16_F32", 512, 256, 64, 1, 2, 0.0, 0.75, seed=3)
@@ -135,6 +153,9 @@ def test_run_errors():
         for bad in (0, 1025):
             with pytest.raises(dg.DistGemmError):
                 dg.dist_gemm_set_option(p.handle, "STEP_GROUP", bad)
+        for bad in (-1, 3):
+            with pytest.raises(dg.DistGemmError):
+                dg.dist_gemm_set_option(p.handle, "COPY_ENGINE", bad)
         with pytest.raises(ValueError):
             p.run(A[:10], A, D, D, 1.0, 1.0)               # too small for 64 x 64
     with pytest.raises(dg.DistGemmError) as ei:

@@ -42,9 +42,10 @@ def test_full_config(name):
     D1 = run_plan(w, x, dev=dev, options={"COMPUTE_STREAMS": 1})
     assert torch.equal(D, D1), "two compute streams != one"
     del D1
-    Db = run_plan(w, x, dev=dev, options={"COPY_ENGINE": 1})
-    assert torch.equal(D, Db), "SDMA copies != default copies"
-    del Db
+    for e in (0, 1, 2):
+        Db = run_plan(w, x, dev=dev, options={"COPY_ENGINE": e})
+        assert torch.equal(D, Db), f"copy engine {e} != the default"
+        del Db
     for n in (1, 7):
         Dn = run_plan(w, x, dev=dev, options={"COPY_STREAMS": n})
         assert torch.equal(D, Dn), f"{n} copy streams != the default"
