@@ -50,7 +50,7 @@ class Step(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m communication_tensor_gemm_amd.build`")
+            f"{LIB_PATH} is not built; run `python communication_tensor_gemm_amd/build.py`")
     # One HIP runtime per process: torch's ROCm build loads its own
     # libamdhip64 (soname libamdhip64.so.7) through an unversioned dependency.
     # Loading torch first makes this library's libamdhip64.so.7 dependency

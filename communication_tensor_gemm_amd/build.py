@@ -1,6 +1,8 @@
 """Build libdistgemm.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m communication_tensor_gemm_amd.build
+    python communication_tensor_gemm_amd/build.py
+
+(By path: importing the package needs the library this builds.)
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ EXTRA = {
     # the fp32 half slab is 256 MFMAs long; without a higher threshold the
     # unroller gives up and the accumulators become a stack array
     "gemm_mfma16.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"],
+    # same guard for the fp8 unit's fully unrolled slab and epilogue
+    "gemm_mfma_f8.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"],
 }
 ARCH = "gfx950"
 
