@@ -135,10 +135,11 @@ def parity_spot_check(w, x, D):
 KERNEL_SOURCES = ["communication_tensor_gemm_amd/csrc/distgemm.hip",
                   "communication_tensor_gemm_amd/csrc/gemm_tile.h",
                   "communication_tensor_gemm_amd/csrc/gemm_launch.h",
+                  "communication_tensor_gemm_amd/csrc/fused_run.h",
                   "communication_tensor_gemm_amd/csrc/gemm_mfma16.hip",
                   "communication_tensor_gemm_amd/csrc/gemm_mfma_f8.hip",
                   "communication_tensor_gemm_amd/build.py"]
-TRAFFIC_FILE = "profiles/gemm_tn_kernel_hbm_traffic.txt"
+TRAFFIC_FILE = "profiles/fused_run_kernel_hbm_traffic.txt"
 
 
 def kernel_source_hash():
@@ -189,6 +190,11 @@ def main():
                     help="0 SDMA, 1 runtime device copy, 2 library copy kernel (default)")
     ap.add_argument("--copy-streams", type=int, default=2, help="side streams for the shard copies (1..8)")
     ap.add_argument("--step-group", type=int, default=2, help="consecutive staged steps per GEMM launch")
+    ap.add_argument("--execution", type=int, default=1,
+                    help="0 = step launches + side-stream copies, 1 = one persistent launch per run")
+    ap.add_argument("--queues", type=int, default=8, help="work queues of the single launch (1 or 8)")
+    ap.add_argument("--copy-chunk", type=int, default=2 << 20, help="bytes per copy item of the single launch")
+    ap.add_argument("--copy-ahead", type=int, default=2, help="copy lookahead of the single launch (groups)")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
@@ -232,6 +238,10 @@ def main():
     plan.set_option("COPY_ENGINE", args.copy_engine)
     plan.set_option("COPY_STREAMS", args.copy_streams)
     plan.set_option("STEP_GROUP", args.step_group)
+    plan.set_option("EXECUTION", args.execution)
+    plan.set_option("QUEUES", args.queues)
+    plan.set_option("COPY_CHUNK", args.copy_chunk)
+    plan.set_option("COPY_AHEAD", args.copy_ahead)
     run_args = (A, B, C if w.beta != 0 else None, D, w.alpha, w.beta)
     log(f"[bench] timing {args.steps} runs after {args.warmup} warmup runs")
     ms, step_ms, run_stats = timed_runs(plan, run_args, args.steps, args.warmup, True)
@@ -279,6 +289,7 @@ def main():
                 "exposed_overhead": ms / mono_ms - 1.0}
         log(f"[bench] monolithic {mono_ms:.3f} ms ({mono['tflops']:.1f} TFLOP/s); "
             f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
+    wait_timeouts = plan.device_errors()
     plan.close()
     del A, B, C, D
     torch.cuda.empty_cache()
@@ -307,12 +318,16 @@ def main():
                    "L": w.L, "TP": w.TP, "in": w.in_dtype, "out": w.out_dtype,
                    "alpha": w.alpha, "beta": w.beta, "compute_streams": args.compute_streams,
                    "copy_engine": ["sdma", "runtime_device_copy", "copy_kernel"][args.copy_engine],
-                   "copy_streams": args.copy_streams, "step_group": args.step_group},
+                   "copy_streams": args.copy_streams, "step_group": args.step_group,
+                   "execution": ["step_launches", "single_launch"][args.execution],
+                   "queues": args.queues, "copy_chunk": args.copy_chunk,
+                   "copy_ahead": args.copy_ahead},
         "pct_mfma_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": recorded_traffic(w.name),
-                     "kernel": "gemm_tn_kernel (step GEMM launches)",
+                     "kernel": ("gemm_tn_kernel (step GEMM launches)" if args.execution == 0 else
+                                "fused_run_kernel (one launch: shard copies and step GEMMs)"),
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch": flops_per_launch, "launches_per_run": n_launch,
                      "gemm_busy_ms": round(busy, 4),
@@ -323,6 +338,7 @@ def main():
         "run_ms": {k: round(v, 4) for k, v in run_stats.items()},
         "monolithic": mono,
         "parity": parity,
+        "device_wait_timeouts": wait_timeouts,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

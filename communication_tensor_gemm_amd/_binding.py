@@ -18,7 +18,8 @@ SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_
              "MONOLITHIC": 4}
 DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4}
 OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2, "COPY_STREAMS": 3,
-           "STEP_GROUP": 4}
+           "STEP_GROUP": 4, "EXECUTION": 5, "QUEUES": 6, "COPY_CHUNK": 7, "WAIT_LIMIT_US": 8,
+           "COPY_AHEAD": 9}
 # bytes per element of (A/B, C/D) for each dtype
 ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
               "E4M3_F32": (1, 4)}
@@ -27,8 +28,8 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM",
 # C functions declared in include/distgemm.h (checked by the CPU tests)
 C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
                "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
-               "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_destroy",
-               "dist_gemm_last_error", "dist_gemm_status_string")
+               "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
+               "dist_gemm_destroy", "dist_gemm_last_error", "dist_gemm_status_string")
 
 
 class DistGemmError(RuntimeError):
@@ -68,6 +69,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_plan_steps.argtypes = [vp, ctypes.POINTER(Step), ctypes.POINTER(i32)]
     lib.dist_gemm_step_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.dist_gemm_step_timeline.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.dist_gemm_device_errors.argtypes = [vp, ctypes.POINTER(i64)]
     lib.dist_gemm_destroy.argtypes = [vp]
     lib.dist_gemm_last_error.argtypes = [vp]
     lib.dist_gemm_last_error.restype = ctypes.c_char_p
@@ -75,7 +77,8 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
     for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
                  "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
-                 "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_destroy"):
+                 "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
+                 "dist_gemm_destroy"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -165,6 +168,13 @@ def dist_gemm_step_timeline(plan) -> List[tuple]:
     return [tuple(buf[3 * s + k] for k in range(3)) for s in range(n.value // 3)]
 
 
+def dist_gemm_device_errors(plan) -> int:
+    """Timed-out device-side shard waits of the plan's single-launch runs so far."""
+    n = ctypes.c_int64(0)
+    _check(lib.dist_gemm_device_errors(plan, ctypes.byref(n)), plan)
+    return n.value
+
+
 def dist_gemm_destroy(plan):
     _check(lib.dist_gemm_destroy(plan))
 
@@ -192,6 +202,9 @@ class Plan:
 
     def step_timeline(self):
         return dist_gemm_step_timeline(self.handle)
+
+    def device_errors(self):
+        return dist_gemm_device_errors(self.handle)
 
     def _need(self, t, nbytes, name):
         if t is None or isinstance(t, int):

@@ -25,6 +25,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -190,6 +191,20 @@ struct dist_gemm_plan_s {
   // [run % step_timing][step] = first step of the launch that computed it
   // (launch events are recorded at that step's index).
   std::vector<int> t_first;
+  // Single-launch execution: device tables and counters (rotating plans only).
+  int execution = 1;
+  int queues = dg::kMaxQueues;
+  int64_t copy_chunk = 2 << 20;
+  int64_t wait_limit_us = 1000000;
+  int64_t clock_khz = 100000;  // device wall clock rate
+  int n_cu = 256;
+  dg::FusedStep* d_steps = nullptr;
+  int32_t* d_seg = nullptr;   // [queues][S + 1] then [queues][S] copy counts
+  int32_t* d_sync = nullptr;
+  uint64_t fused_align = 0;   // OR of the chunk widths (copy unit choice)
+  int fused_groups = 0;       // launch groups in the device tables
+  int copy_ahead = 2;         // copy lookahead, launch groups
+  std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
   int compute_streams = 2;
   int copy_engine = 2;  // library streaming copy kernel
@@ -231,6 +246,9 @@ void release(dist_gemm_plan_s* p) {
   for (hipStream_t s : p->sides) if (s) (void)hipStreamDestroy(s);
   if (p->cs2) (void)hipStreamDestroy(p->cs2);
   if (p->staging) (void)hipFree(p->staging);
+  if (p->d_steps) (void)hipFree(p->d_steps);
+  if (p->d_seg) (void)hipFree(p->d_seg);
+  if (p->d_sync) (void)hipFree(p->d_sync);
   delete p;
 }
 
@@ -365,44 +383,64 @@ std::vector<LaunchGroup> group_steps(const dist_gemm_plan_s* P) {
   return v;
 }
 
-// GEMM parameters of one step.
-dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, const void* A,
-                           const void* B, const void* C, void* D, float alpha, float beta) {
+// Where step st's operands live: byte offsets from the caller's operands,
+// or (staged*) from the staging buffer, with leading dimensions and batch
+// strides in elements.
+struct StepLayout {
+  int64_t offA, offB, offC, offD;
+  int64_t lda, ldb, ldc, ldd, sA, sB, sC, sD;
+  int32_t M, N;
+  bool stagedA, stagedB, stagedC;
+};
+
+StepLayout step_layout(const dist_gemm_plan_s* P, const dist_gemm_step& st) {
   const Problem& pr = P->pr;
   const int64_t M = pr.M, N = pr.N, K = pr.K;
   const int64_t S = pr.S;
   const int ei = pr.es_in, eo = pr.es_out;
-  const uint8_t* a = static_cast<const uint8_t*>(A);
-  const uint8_t* b = static_cast<const uint8_t*>(B);
-  const uint8_t* c = static_cast<const uint8_t*>(C);
-  uint8_t* d = static_cast<uint8_t*>(D);
-  const uint8_t* slot =
-      st.staged ? P->staging + static_cast<size_t>(st.slot) * P->geom.width : nullptr;
+  const int64_t slot = st.staged ? static_cast<int64_t>(st.slot) * P->geom.width : 0;
   const int64_t slots = S - 1;
-
-  dg::GemmParams g{};
-  g.K = static_cast<int32_t>(K);
-  g.L = static_cast<int32_t>(pr.L);
-  g.alpha = alpha;
-  g.beta = beta;
-  g.M = static_cast<int32_t>(st.m1 - st.m0);
-  g.N = static_cast<int32_t>(st.n1 - st.n0);
+  StepLayout y{};
+  y.M = static_cast<int32_t>(st.m1 - st.m0);
+  y.N = static_cast<int32_t>(st.n1 - st.n0);
   // defaults: operands in place
-  g.A = a + (st.m0 * K) * ei;  g.lda = K; g.sA = M * K;
-  g.B = b + (st.n0 * K) * ei;  g.ldb = K; g.sB = N * K;
-  g.C = c ? c + (st.m0 * N + st.n0) * eo : nullptr; g.ldc = N; g.sC = M * N;
-  g.D = d + (st.m0 * N + st.n0) * eo; g.ldd = N; g.sD = M * N;
+  y.offA = st.m0 * K * ei;  y.lda = K; y.sA = M * K;
+  y.offB = st.n0 * K * ei;  y.ldb = K; y.sB = N * K;
+  y.offC = (st.m0 * N + st.n0) * eo; y.ldc = N; y.sC = M * N;
+  y.offD = (st.m0 * N + st.n0) * eo; y.ldd = N; y.sD = M * N;
   if (st.staged) {
     switch (pr.schedule) {
-      case DIST_GEMM_AG_ROT_A: g.A = slot; g.sA = slots * (M / S) * K; break;
-      case DIST_GEMM_AG_ROT_B: g.B = slot; g.sB = slots * (N / S) * K; break;
-      case DIST_GEMM_RS_TILE_A_ROT_C: g.C = slot; g.ldc = N; g.sC = slots * (M / S) * N; break;
+      case DIST_GEMM_AG_ROT_A: y.stagedA = true; y.offA = slot; y.sA = slots * (M / S) * K; break;
+      case DIST_GEMM_AG_ROT_B: y.stagedB = true; y.offB = slot; y.sB = slots * (N / S) * K; break;
+      case DIST_GEMM_RS_TILE_A_ROT_C:
+        y.stagedC = true; y.offC = slot; y.ldc = N; y.sC = slots * (M / S) * N; break;
       case DIST_GEMM_RS_TILE_B_ROT_C:
-        g.C = slot; g.ldc = slots * (N / S); g.sC = M * slots * (N / S); break;
+        y.stagedC = true; y.offC = slot; y.ldc = slots * (N / S); y.sC = M * slots * (N / S); break;
       default: break;
     }
   }
-  if (beta == 0.0f) g.C = nullptr;
+  return y;
+}
+
+// GEMM parameters of one step.
+dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, const void* A,
+                           const void* B, const void* C, void* D, float alpha, float beta) {
+  const StepLayout y = step_layout(P, st);
+  const uint8_t* stg = P->staging;
+  dg::GemmParams g{};
+  g.K = static_cast<int32_t>(P->pr.K);
+  g.L = static_cast<int32_t>(P->pr.L);
+  g.alpha = alpha;
+  g.beta = beta;
+  g.M = y.M;
+  g.N = y.N;
+  g.A = (y.stagedA ? stg : static_cast<const uint8_t*>(A)) + y.offA;
+  g.B = (y.stagedB ? stg : static_cast<const uint8_t*>(B)) + y.offB;
+  g.C = (beta == 0.0f || (!y.stagedC && !C)) ? nullptr
+                                             : (y.stagedC ? stg : static_cast<const uint8_t*>(C)) + y.offC;
+  g.D = static_cast<uint8_t*>(D) + y.offD;
+  g.lda = y.lda; g.ldb = y.ldb; g.ldc = y.ldc; g.ldd = y.ldd;
+  g.sA = y.sA; g.sB = y.sB; g.sC = y.sC; g.sD = y.sD;
   return g;
 }
 
@@ -418,6 +456,162 @@ dg::GemmParams group_params(const dist_gemm_plan_s* P, const LaunchGroup& grp, c
   g.M = static_cast<int32_t>(std::max(f.m1, l.m1) - f.m0);
   g.N = static_cast<int32_t>(std::max(f.n1, l.n1) - f.n0);
   return g;
+}
+
+// ---- Single-launch execution ----------------------------------------------
+
+// Build the device tables of the single-launch run: the pointer-free table of
+// launch groups with their copy chunking, each queue's tile segments, and
+// zeroed counters.  Synchronous (plan creation and option changes only).
+int build_fused(dist_gemm_plan_s* P, std::string* err) {
+  const Problem& pr = P->pr;
+  const int S = pr.S;
+  const int nq = P->queues;
+  const CopyGeom& cg = P->geom;
+  const int64_t width = static_cast<int64_t>(cg.width), height = static_cast<int64_t>(cg.height);
+
+  // one table entry per launch group (the step-launch execution's grouping)
+  const std::vector<LaunchGroup> groups = group_steps(P);
+  const int G = static_cast<int>(groups.size());
+  std::vector<dg::FusedStep> fs(G);
+  for (int gi = 0; gi < G; ++gi) {
+    const LaunchGroup& grp = groups[gi];
+    const dist_gemm_step& st = P->steps[grp.first];
+    const dist_gemm_step& last = P->steps[grp.first + grp.count - 1];
+    const StepLayout y = step_layout(P, st);
+    dg::FusedStep& f = fs[gi];
+    f.offA = y.offA; f.offB = y.offB; f.offC = y.offC; f.offD = y.offD;
+    f.lda = y.lda; f.ldb = y.ldb; f.ldc = y.ldc; f.ldd = y.ldd;
+    f.sA = y.sA; f.sB = y.sB; f.sC = y.sC; f.sD = y.sD;
+    f.M = static_cast<int32_t>(std::max(st.m1, last.m1) - st.m0);
+    f.N = static_cast<int32_t>(std::max(st.n1, last.n1) - st.n0);
+    f.tiles_m = (f.M + dg::kBM - 1) / dg::kBM;
+    f.tiles_n = (f.N + dg::kBN - 1) / dg::kBN;
+    f.stagedA = y.stagedA; f.stagedB = y.stagedB; f.stagedC = y.stagedC;
+    f.copy_src_off = st.staged ? static_cast<int64_t>(st.shard) * width : 0;
+    f.copy_dst_off = st.staged ? static_cast<int64_t>(st.slot) * width : 0;
+  }
+  // Copy chunking of group h: its bytes spread over the tiles of its carrier
+  // group max(0, h - D), about one chunk per tile (at most COPY_CHUNK bytes,
+  // at least 4 KiB, a multiple of 16), so that every carrier does about the
+  // same copy work.
+  for (int h = 0; h < G; ++h) {
+    dg::FusedStep& f = fs[h];
+    f.chunk_cols = width; f.chunk_rows = 1; f.chunks_per_row = 1; f.chunks_per_step = 0;
+    f.n_chunks = 0;
+    if (!P->steps[groups[h].first].staged) continue;
+    const dg::FusedStep& carrier = fs[std::max(0, h - P->copy_ahead)];
+    const int64_t ctiles = static_cast<int64_t>(carrier.tiles_m) * carrier.tiles_n * pr.L;
+    const int64_t bytes = width * height * groups[h].count;
+    int64_t chunk = (bytes + ctiles - 1) / ctiles;
+    chunk = std::min<int64_t>(P->copy_chunk, std::max<int64_t>(4096, (chunk + 15) / 16 * 16));
+    if (width >= chunk) {
+      f.chunk_cols = chunk;
+      f.chunks_per_row = static_cast<int32_t>((width + chunk - 1) / chunk);
+      f.chunk_rows = 1;
+    } else {
+      f.chunk_cols = width;
+      f.chunks_per_row = 1;
+      f.chunk_rows = std::max<int64_t>(1, chunk / width);
+    }
+    const int64_t per_step = (height + f.chunk_rows - 1) / f.chunk_rows * f.chunks_per_row;
+    if (per_step * groups[h].count > (int64_t{1} << 30))
+      return fail(err, DIST_GEMM_ERR_UNSUPPORTED, "too many copy chunks; raise DIST_GEMM_OPT_COPY_CHUNK");
+    f.chunks_per_step = static_cast<int32_t>(per_step);
+    f.n_chunks = static_cast<int32_t>(per_step * groups[h].count);
+  }
+  P->fused_groups = G;
+  // queue q: its share of every group's tiles (a contiguous range of the
+  // group's tile order per batch), group after group
+  std::vector<int32_t> seg(static_cast<size_t>(nq) * (G + 1), 0);
+  for (int q = 0; q < nq; ++q) {
+    int64_t at = 0;
+    for (int s = 0; s < G; ++s) {
+      seg[static_cast<size_t>(q) * (G + 1) + s] = static_cast<int32_t>(at);
+      const int64_t T2 = static_cast<int64_t>(fs[s].tiles_m) * fs[s].tiles_n;
+      at += (T2 / nq + (q < T2 % nq ? 1 : 0)) * pr.L;
+      if (at >= INT32_MAX || T2 * pr.L >= INT32_MAX)
+        return fail(err, DIST_GEMM_ERR_SHAPE, "too many tiles for one launch");
+    }
+    seg[static_cast<size_t>(q) * (G + 1) + G] = static_cast<int32_t>(at);
+  }
+  const size_t sync_words = static_cast<size_t>(dg::kSyncDone + S) * dg::kSyncStride;
+  if (!P->d_steps) DG_HIP(err, hipMalloc(&P->d_steps, sizeof(dg::FusedStep) * S));
+  if (P->d_seg) {
+    DG_HIP(err, hipFree(P->d_seg));
+    P->d_seg = nullptr;
+  }
+  DG_HIP(err, hipMalloc(&P->d_seg, seg.size() * sizeof(int32_t)));
+  if (!P->d_sync) {
+    DG_HIP(err, hipMalloc(&P->d_sync, sync_words * sizeof(int32_t)));
+    DG_HIP(err, hipMemset(P->d_sync, 0, sync_words * sizeof(int32_t)));
+  }
+  DG_HIP(err, hipMemcpy(P->d_steps, fs.data(), sizeof(dg::FusedStep) * G, hipMemcpyHostToDevice));
+  DG_HIP(err, hipMemcpy(P->d_seg, seg.data(), seg.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  P->fused_align = 0;
+  for (const dg::FusedStep& f : fs) P->fused_align |= static_cast<uint64_t>(f.chunk_cols);
+  return DIST_GEMM_OK;
+}
+
+// Single-launch runs on one device are ordered one after another, across
+// plans: the last one's completion event per device.
+struct FusedOrder {
+  std::mutex mu;
+  std::vector<hipEvent_t> tail;  // per device, created on first use
+  std::vector<char> live;
+};
+FusedOrder& fused_order() {
+  static FusedOrder* o = new FusedOrder();  // never destroyed: outlives every plan
+  return *o;
+}
+
+int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B, const void* C,
+              void* D, float alpha, float beta, const void* copy_src) {
+  const Problem& pr = P->pr;
+  const CopyGeom& g = P->geom;
+  dg::FusedArgs a{};
+  a.A = A; a.B = B; a.C = beta != 0.0f ? C : nullptr; a.D = D;
+  a.staging = P->staging;
+  a.copy_src = copy_src;
+  a.steps = P->d_steps;
+  a.seg = P->d_seg;
+  a.sync = P->d_sync;
+  a.cp_width = static_cast<int64_t>(g.width);
+  a.cp_height = static_cast<int64_t>(g.height);
+  a.cp_src_pitch = static_cast<int64_t>(g.src_pitch);
+  a.cp_dst_pitch = static_cast<int64_t>(P->staging_pitch);
+  a.spin_limit = P->wait_limit_us * P->clock_khz / 1000;
+  const uint64_t align = reinterpret_cast<uint64_t>(copy_src) | reinterpret_cast<uint64_t>(P->staging) |
+                         g.src_pitch | P->staging_pitch | g.width | P->fused_align;
+  a.unit = (align % 16 == 0) ? 16 : (align % 4 == 0) ? 4 : 1;
+  a.S = P->fused_groups;
+  a.K = static_cast<int32_t>(pr.K);
+  a.L = static_cast<int32_t>(pr.L);
+  a.nq = P->queues;
+  a.ahead = P->copy_ahead;
+  a.alpha = alpha;
+  a.beta = beta;
+  const int grid = std::max(P->queues, P->n_cu / P->queues * P->queues);
+
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  DG_HIP(&P->err, hipStreamIsCapturing(st, &cap));
+  const bool ordered = cap == hipStreamCaptureStatusNone;
+  FusedOrder& o = fused_order();
+  std::unique_lock<std::mutex> lock(o.mu);
+  if (ordered) {
+    if (static_cast<int>(o.tail.size()) <= P->device) {
+      o.tail.resize(P->device + 1, nullptr);
+      o.live.resize(P->device + 1, 0);
+    }
+    if (!o.tail[P->device]) DG_HIP(&P->err, hipEventCreateWithFlags(&o.tail[P->device], hipEventDisableTiming));
+    if (o.live[P->device]) DG_HIP(&P->err, hipStreamWaitEvent(st, o.tail[P->device], 0));
+  }
+  DG_HIP(&P->err, dg::launch_fused(pr.in_kind, pr.out_kind, a, grid, st));
+  if (ordered) {
+    DG_HIP(&P->err, hipEventRecord(o.tail[P->device], st));
+    o.live[P->device] = 1;
+  }
+  return DIST_GEMM_OK;
 }
 
 }  // namespace
@@ -505,6 +699,17 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
     release(P);
     return rc;
   }
+  P->n_cu = std::max(1, prop.multiProcessorCount);
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    P->clock_khz = khz;
+  if (pr.schedule != DIST_GEMM_MONOLITHIC && n_slots > 0) {
+    rc = build_fused(P, perr);
+    if (rc != DIST_GEMM_OK) {
+      release(P);
+      return rc;
+    }
+  }
   *out = P;
   return DIST_GEMM_OK;
 }
@@ -541,10 +746,73 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       plan->copy_streams = static_cast<int>(value);
       return DIST_GEMM_OK;
     }
-    case DIST_GEMM_OPT_STEP_GROUP:
+    case DIST_GEMM_OPT_STEP_GROUP: {
       if (value < 1 || value > 1024)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "step group must be 1..1024");
+      if (plan->max_group == value) return DIST_GEMM_OK;
+      const int old_g = plan->max_group;
       plan->max_group = static_cast<int>(value);
+      if (!plan->d_steps) return DIST_GEMM_OK;
+      DeviceGuard guard(plan->device);
+      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+      const int rc = build_fused(plan, &plan->err);
+      if (rc != DIST_GEMM_OK) {
+        plan->max_group = old_g;
+        (void)build_fused(plan, nullptr);
+      }
+      return rc;
+    }
+    case DIST_GEMM_OPT_EXECUTION:
+      if (value != 0 && value != 1)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "execution must be 0 or 1");
+      plan->execution = static_cast<int>(value);
+      return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_QUEUES:
+    case DIST_GEMM_OPT_COPY_CHUNK: {
+      const bool queues = option == DIST_GEMM_OPT_QUEUES;
+      if (queues && value != 1 && value != dg::kMaxQueues)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "queues must be 1 or 8");
+      if (!queues && (value < 4096 || value > (int64_t{1} << 28) || value % 16 != 0))
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG,
+                    "copy chunk must be a multiple of 16 in [4096, 2^28]");
+      if ((queues ? plan->queues : plan->copy_chunk) == value) return DIST_GEMM_OK;
+      const int old_q = plan->queues;
+      const int64_t old_c = plan->copy_chunk;
+      if (queues)
+        plan->queues = static_cast<int>(value);
+      else
+        plan->copy_chunk = value;
+      if (!plan->d_steps) return DIST_GEMM_OK;  // no staged steps: nothing to rebuild
+      DeviceGuard guard(plan->device);
+      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+      const int rc = build_fused(plan, &plan->err);
+      if (rc != DIST_GEMM_OK) {
+        plan->queues = old_q;
+        plan->copy_chunk = old_c;
+        (void)build_fused(plan, nullptr);
+      }
+      return rc;
+    }
+    case DIST_GEMM_OPT_COPY_AHEAD: {
+      if (value < 1 || value > 1024)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy lookahead must be 1..1024");
+      if (plan->copy_ahead == value) return DIST_GEMM_OK;
+      const int old_a = plan->copy_ahead;
+      plan->copy_ahead = static_cast<int>(value);
+      if (!plan->d_steps) return DIST_GEMM_OK;
+      DeviceGuard guard(plan->device);
+      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+      const int rc = build_fused(plan, &plan->err);
+      if (rc != DIST_GEMM_OK) {
+        plan->copy_ahead = old_a;
+        (void)build_fused(plan, nullptr);
+      }
+      return rc;
+    }
+    case DIST_GEMM_OPT_WAIT_LIMIT_US:
+      if (value < 0 || value > 100000000)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "wait limit must be in [0, 1e8] us");
+      plan->wait_limit_us = value;
       return DIST_GEMM_OK;
     case DIST_GEMM_OPT_STEP_TIMING: {
       if (value < 0 || value > 4096)
@@ -556,6 +824,7 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       for (hipEvent_t ev : plan->t_run0) if (ev) (void)hipEventDestroy(ev);
       for (hipEvent_t ev : plan->t_copy) if (ev) (void)hipEventDestroy(ev);
       plan->t_first.clear();
+      plan->t_fused.clear();
       plan->t_begin.clear();
       plan->t_end.clear();
       plan->t_run0.clear();
@@ -567,6 +836,7 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       plan->t_end.assign(n, nullptr);
       plan->t_copy.assign(n, nullptr);
       plan->t_first.assign(n, 0);
+      plan->t_fused.assign(static_cast<size_t>(value), 0);
       plan->t_run0.assign(static_cast<size_t>(value), nullptr);
       for (size_t i = 0; i < n; ++i) {
         hipError_t e = hipEventCreate(&plan->t_begin[i]);
@@ -614,6 +884,26 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
                 "the reduce-scatter schedules rotate C: C must be non-NULL");
   }
 
+  if (rotating && P->execution == 1) {
+    if (P->has_prev && P->prev_stream != st) DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_done, 0));
+    const size_t trun = P->step_timing ? static_cast<size_t>(P->timed_runs % P->step_timing) : 0;
+    const size_t tbase = trun * P->steps.size();
+    if (P->step_timing) {
+      DG_HIP(&P->err, hipEventRecord(P->t_run0[trun], st));
+      for (size_t k = 0; k < P->steps.size(); ++k) P->t_first[tbase + k] = 0;
+      P->t_fused[trun] = 1;
+      DG_HIP(&P->err, hipEventRecord(P->t_begin[tbase], st));
+    }
+    const int rc = run_fused(P, st, A, B, C, D, alpha_eff, beta, copy_src);
+    if (rc != DIST_GEMM_OK) return rc;
+    if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[tbase], st));
+    DG_HIP(&P->err, hipEventRecord(P->ev_done, st));
+    P->has_prev = true;
+    P->prev_stream = st;
+    if (P->step_timing) ++P->timed_runs;
+    return DIST_GEMM_OK;
+  }
+
   // side streams in use: the first n, n = min(copy streams, staged copies)
   const int n_side = rotating ? std::min(P->copy_streams, pr.S - 1) : 0;
   if (n_side > static_cast<int>(P->sides.size()))
@@ -623,7 +913,10 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
   DG_HIP(&P->err, hipEventRecord(P->ev_start, st));
   const size_t trun = P->step_timing ? static_cast<size_t>(P->timed_runs % P->step_timing) : 0;
   const size_t tbase = trun * P->steps.size();
-  if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_run0[trun], st));
+  if (P->step_timing) {
+    DG_HIP(&P->err, hipEventRecord(P->t_run0[trun], st));
+    P->t_fused[trun] = 0;
+  }
   for (int k = 0; k < n_side; ++k) DG_HIP(&P->err, hipStreamWaitEvent(P->sides[k], P->ev_start, 0));
   if (two) DG_HIP(&P->err, hipStreamWaitEvent(P->cs2, P->ev_start, 0));
 
@@ -719,7 +1012,8 @@ int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n) {
   hipEvent_t t0 = plan->t_run0[run];
   for (int64_t s = 0; s < S; ++s) {
     float v[3] = {-1.0f, 0.0f, 0.0f};
-    const bool staged = plan->steps[s].staged && plan->pr.schedule != DIST_GEMM_MONOLITHIC;
+    const bool staged = plan->steps[s].staged && plan->pr.schedule != DIST_GEMM_MONOLITHIC &&
+                        !plan->t_fused[run];
     if (staged) DG_HIP(&plan->err, hipEventElapsedTime(&v[0], t0, plan->t_copy[base + s]));
     const int f = plan->t_first[base + s];
     DG_HIP(&plan->err, hipEventElapsedTime(&v[1], t0, plan->t_begin[base + f]));
@@ -728,6 +1022,19 @@ int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n) {
       if (3 * s + k < cap) ms[3 * s + k] = v[k];
   }
   *n = static_cast<int>(3 * S);
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_device_errors(dist_gemm_plan_t plan, int64_t* count) {
+  if (!plan || !count) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan or count is NULL");
+  *count = 0;
+  if (!plan->d_sync) return DIST_GEMM_OK;
+  DeviceGuard guard(plan->device);
+  if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+  int32_t v = 0;
+  const size_t at = static_cast<size_t>(dg::kSyncErr) * dg::kSyncStride;
+  DG_HIP(&plan->err, hipMemcpy(&v, plan->d_sync + at, sizeof(v), hipMemcpyDeviceToHost));
+  *count = v;
   return DIST_GEMM_OK;
 }
 

@@ -45,7 +45,7 @@
 //
 // Workgroup -> tile mapping is XCD-aware: MI355X places workgroup b on XCD
 // b mod 8, so each XCD gets one contiguous range of the tile order, and
-// that order walks groups of 8 tile rows column by column, so the tiles an
+// that order walks groups of kGroupM tile rows column by column, so the tiles an
 // XCD runs together share A rows and B columns in its own L2.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -99,11 +99,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  const int x = bid % kNumXcd, i = bid / kNumXcd;
-  const int q = T / kNumXcd, r = T % kNumXcd;
-  const int t = x * q + min(x, r) + i;
+// Position t of the tile order -> tile (tm, tn): groups of kGroupM tile rows,
+// each walked column by column.
+__device__ __forceinline__ void order_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int g = t / per_group;
   const int first_m = g * kGroupM;
@@ -111,6 +109,14 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
   const int w = t - g * per_group;
   tm = first_m + w % gm;
   tn = w / gm;
+}
+
+// Workgroup bid -> tile: XCD bid mod 8 takes one contiguous range of the order.
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int x = bid % kNumXcd, i = bid / kNumXcd;
+  const int q = T / kNumXcd, r = T % kNumXcd;
+  order_tile(x * q + min(x, r) + i, tiles_m, tiles_n, tm, tn);
 }
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
@@ -440,22 +446,16 @@ __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lan
   }
 }
 
+// One 256 x 256 tile (tm, tn) of batch l of the GEMM p, computed by the
+// whole workgroup with the LDS ring smem.  Every argument is workgroup-uniform.
 template <int IN, int OUT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-gemm_tn_kernel(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, int tn, uint8_t* smem) {
   using M = Mma<IN>;
   constexpr int ES = elem_size<IN>();
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * kOperandSlab];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int l = blockIdx.y;
-
-  const int tiles_m = (p.M + kBM - 1) / kBM;
-  const int tiles_n = (p.N + kBN - 1) / kBN;
-  int tm, tn;
-  map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
 
   TileCtx c;
@@ -594,6 +594,17 @@ gemm_tn_kernel(GemmParams p) {
     }
   }
   epilogue_direct<M, OUT>(elane, acc, p, Dw, Cw, rows_left, cols_left);
+}
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+gemm_tn_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * kOperandSlab];
+  const int tiles_m = (p.M + kBM - 1) / kBM;
+  const int tiles_n = (p.N + kBN - 1) / kBN;
+  int tm, tn;
+  map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  gemm_tile<IN, OUT>(p, blockIdx.y, tm, tn, smem);
 }
 
 template <int IN, int OUT>

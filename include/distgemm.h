@@ -155,18 +155,52 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
  *     (with the two compute streams, four streams: the hardware queues a
  *     process gets by default).
  *   DIST_GEMM_OPT_STEP_GROUP: g in 1..1024 = at most g consecutive staged
- *     steps run as one GEMM launch once all of their shards have arrived.
+ *     steps run as one GEMM (one launch in mode 0, one group of tiles in
+ *     mode 1) once all of their shards have arrived.
  *     Consecutive steps consume adjacent shards (rows of A, columns of B or
  *     of the partial) that sit in adjacent staging slots, so their GEMMs
  *     are one GEMM over the union; every output element is computed exactly
  *     as by its own step.  The step that uses the local shard launches
- *     alone.  1 = one launch per step; default 2. */
+ *     alone.  1 = one launch per step; default 2.
+ *   DIST_GEMM_OPT_EXECUTION: how a run with more than one step executes.
+ *     0 = step launches and side-stream copies (the options above apply);
+ *     1 (default) = one persistent launch on the caller's stream does
+ *     the whole run: its workgroups compute the step tiles, every tile
+ *     first copying an equal chunk of a later step's shard, and a tile of a
+ *     staged step starts once a device-side counter shows its step's shard
+ *     complete (the per-step ready barrier of the Distributed GEMM
+ *     pull-request page, kept on the device).  Every element is computed exactly as in mode 0 (same
+ *     kernel tile, same K order).  Single-launch runs on one device are
+ *     ordered after one another, also across plans (their workgroups must
+ *     not wait on each other), except inside a graph capture.
+ *   DIST_GEMM_OPT_QUEUES (mode 1): 8 (default) = one work queue per XCD,
+ *     each XCD runs contiguous ranges of every step's tile order; 1 = one
+ *     queue for the chip.
+ *   DIST_GEMM_OPT_COPY_CHUNK (mode 1): the largest copy chunk one tile
+ *     carries, in bytes, a multiple of 16 in [4096, 2^28]; default 2 MiB.
+ *     A step's shard is spread over the tiles of the group D before it in
+ *     chunks of about equal size (shard bytes / tiles), capped by this.  The plan's device tables are
+ *     rebuilt (synchronously) when it changes.
+ *   DIST_GEMM_OPT_WAIT_LIMIT_US (mode 1): how long one wait for a shard may
+ *     last, in microseconds, in [0, 10^8]; default 10^6.  A wait that runs
+ *     out is counted (dist_gemm_device_errors) and the tile proceeds with
+ *     whatever the staging slot holds: the run's result is then undefined.
+ *     In correct operation no wait runs out.
+ *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 1..1024; the chunks of launch
+ *     group h are carried by the tiles of group max(0, h - D), i.e. D
+ *     groups ahead of their use; default 2.  Larger D suits copy-bound
+ *     workloads (partials much larger than the step's arithmetic). */
 enum dist_gemm_option {
   DIST_GEMM_OPT_COMPUTE_STREAMS = 0,
   DIST_GEMM_OPT_COPY_ENGINE = 1,
   DIST_GEMM_OPT_STEP_TIMING = 2,
   DIST_GEMM_OPT_COPY_STREAMS = 3,
-  DIST_GEMM_OPT_STEP_GROUP = 4
+  DIST_GEMM_OPT_STEP_GROUP = 4,
+  DIST_GEMM_OPT_EXECUTION = 5,
+  DIST_GEMM_OPT_QUEUES = 6,
+  DIST_GEMM_OPT_COPY_CHUNK = 7,
+  DIST_GEMM_OPT_WAIT_LIMIT_US = 8,
+  DIST_GEMM_OPT_COPY_AHEAD = 9
 };
 int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
 
@@ -184,7 +218,10 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  * Graph capture: with DIST_GEMM_OPT_STEP_TIMING = 0 and the plan's previous
  * run (if any) on the same stream, a run enqueues only copies, kernel
  * launches and event record / wait pairs that fork from and join back into
- * `stream`, so it can be captured into a HIP graph.  The graph uses the
+ * `stream` (a single-launch run: one kernel launch), so it can be captured
+ * into a HIP graph.  A captured single-launch run is not ordered against
+ * single-launch runs of other plans: do not replay it while one of those
+ * may run on the device.  The graph uses the
  * plan's staging buffer: its replays must not overlap other runs of the
  * plan, and the plan must outlive the graph. */
 int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
@@ -203,10 +240,18 @@ int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n);
 /* With DIST_GEMM_OPT_STEP_TIMING set: wait for the last run to finish and
  * write its timeline, three values per step in step order, in milliseconds
  * since the run was enqueued on its stream: [3s] = the moment the step's
- * shard copy completed (-1 for a step that consumes no copy), [3s+1] = the
- * GEMM launch that computed it began, [3s+2] = it ended.  At most *n values are written; *n
- * receives 3 * steps.  UNSUPPORTED if no timed run exists. */
+ * shard copy completed (-1 for a step that consumes no copy, and for every
+ * step of a single-launch run, whose copies happen inside the launch),
+ * [3s+1] = the GEMM launch that computed it began, [3s+2] = it ended.  At
+ * most *n values are written; *n receives 3 * steps.  UNSUPPORTED if no timed run exists. */
 int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n);
+
+/* Wait for the plan's last run and write to *count the number of device-side
+ * shard waits that ran out of time (DIST_GEMM_OPT_WAIT_LIMIT_US) in all
+ * single-launch runs of the plan so far.  0 in correct operation; a run with
+ * a wait that ran out has an undefined result.  INVALID_ARG for NULL
+ * arguments; HIP if the read fails. */
+int dist_gemm_device_errors(dist_gemm_plan_t plan, int64_t* count);
 
 /* Synchronise the plan's streams, free its staging, streams and events, and
  * the handle.  NULL is accepted (no-op). */

@@ -81,6 +81,10 @@ def test_null_handles_are_rejected_without_gpu():
     assert dg.lib.dist_gemm_plan_steps(None, None, ctypes.byref(n)) == -1
     assert dg.lib.dist_gemm_step_times(None, None, ctypes.byref(n)) == -1
     assert dg.lib.dist_gemm_step_timeline(None, None, ctypes.byref(n)) == -1
+    c = ctypes.c_int64(0)
+    assert dg.lib.dist_gemm_device_errors(None, ctypes.byref(c)) == -1
+    for opt in range(10):
+        assert dg.lib.dist_gemm_set_option(None, opt, 1) == -1
 
 
 def test_single_hip_runtime_in_process():

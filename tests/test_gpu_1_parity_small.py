@@ -67,10 +67,11 @@ def test_edge_shapes(M, N, K, TP, sched, dtype):
     check_full(w, x, D)
 
 
+@pytest.mark.parametrize("execution", [0, 1])
 @pytest.mark.parametrize("group", [2, 3, 8])
 @pytest.mark.parametrize("dtype", ["F32", "BF16_BF16", "E4M3_F32"])
 @pytest.mark.parametrize("sched", ["AG_ROT_A", "AG_ROT_B", "RS_TILE_A_ROT_C", "RS_TILE_B_ROT_C"])
-def test_step_groups(sched, dtype, group):
+def test_step_groups(sched, dtype, group, execution):
     # TP=8 on 600 x 520: 75-row / 65-column shards, so merged launches have
     # tiles that straddle shard boundaries; L=2 exercises the batch strides
     # of the side-by-side staging layout.
@@ -79,11 +80,11 @@ def test_step_groups(sched, dtype, group):
     w = workloads.small_case(f"group_{sched}_{dtype}_{group}", sched, dtype, 600, 520, 96, 2, 8,
                              1.5, beta, seed=group * 7 + len(sched))
     x = workloads.generate(w)
-    log("case", w.name, "STEP_GROUP", group)
+    log("case", w.name, "STEP_GROUP", group, "EXECUTION", execution)
     dev = (to_gpu(x.A), to_gpu(x.B), to_gpu(x.C))
-    Dg = run_plan(w, x, dev=dev, options={"STEP_GROUP": group})
+    Dg = run_plan(w, x, dev=dev, options={"STEP_GROUP": group, "EXECUTION": execution})
     check_full(w, x, Dg)
-    D1 = run_plan(w, x, dev=dev, options={"STEP_GROUP": 1})
+    D1 = run_plan(w, x, dev=dev, options={"STEP_GROUP": 1, "EXECUTION": execution})
     assert torch.equal(Dg, D1), "grouped launches differ from one launch per step"
 
 
@@ -100,9 +101,11 @@ def test_copy_engines_agree(sched, dtype):
     x = workloads.generate(w)
     dev = (to_gpu(x.A), to_gpu(x.B), to_gpu(x.C))
     log("case", w.name)
-    outs = [run_plan(w, x, dev=dev, options={"COPY_ENGINE": e}) for e in (0, 1, 2)]
+    outs = [run_plan(w, x, dev=dev, options={"COPY_ENGINE": e, "EXECUTION": 0}) for e in (0, 1, 2)]
     check_full(w, x, outs[2])
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    # the single launch's own chunked copy (16-, 4- and 1-byte units alike)
+    assert torch.equal(outs[2], run_plan(w, x, dev=dev, options={"EXECUTION": 1}))
 
 
 def test_alpha_zero_and_beta_zero_ignores_c():

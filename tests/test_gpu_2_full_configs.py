@@ -1,11 +1,12 @@
 """GPU parity at the four full-size workloads, in the launch configuration the
-benchmark times (two compute streams, SDMA shard copies).
+benchmark times (the library defaults: one persistent launch per run).
 
 The oracle computes sampled outputs one by one: rows and columns that cover
 every step block, both sides of 256-tile edges, and random positions.  The
 properties that hold at any size are checked on the whole output, bitwise:
-the schedule equals the monolithic GEMM of the same kernel, one compute
-stream equals two, and the runtime's default copy path equals the SDMA one.
+the schedule equals the monolithic GEMM of the same kernel, and the
+step-launch execution with every copy engine, copy-stream count, compute
+stream count and step grouping equals it too.
 """
 import numpy as np
 import pytest
@@ -39,21 +40,23 @@ def test_full_config(name):
     Dm = run_plan(w, x, schedule="MONOLITHIC", TP=1, dev=dev)
     assert torch.equal(D, Dm), "schedule != monolithic"
     del Dm
-    D1 = run_plan(w, x, dev=dev, options={"COMPUTE_STREAMS": 1})
-    assert torch.equal(D, D1), "two compute streams != one"
+    # step-launch execution and its options
+    D1 = run_plan(w, x, dev=dev, options={"EXECUTION": 0, "COMPUTE_STREAMS": 1})
+    assert torch.equal(D, D1), "step launches on one compute stream != the default"
     del D1
     for e in (0, 1, 2):
-        Db = run_plan(w, x, dev=dev, options={"COPY_ENGINE": e})
-        assert torch.equal(D, Db), f"copy engine {e} != the default"
+        Db = run_plan(w, x, dev=dev, options={"EXECUTION": 0, "COPY_ENGINE": e})
+        assert torch.equal(D, Db), f"step launches with copy engine {e} != the default"
         del Db
     for n in (1, 7):
-        Dn = run_plan(w, x, dev=dev, options={"COPY_STREAMS": n})
-        assert torch.equal(D, Dn), f"{n} copy streams != the default"
+        Dn = run_plan(w, x, dev=dev, options={"EXECUTION": 0, "COPY_STREAMS": n})
+        assert torch.equal(D, Dn), f"step launches with {n} copy streams != the default"
         del Dn
     for g in (1, 2, 7):
-        Dg = run_plan(w, x, dev=dev, options={"STEP_GROUP": g})
-        assert torch.equal(D, Dg), f"step groups of {g} != the default"
-        del Dg
+        for ex in (0, 1):
+            Dg = run_plan(w, x, dev=dev, options={"EXECUTION": ex, "STEP_GROUP": g})
+            assert torch.equal(D, Dg), f"execution {ex}, step groups of {g} != the default"
+            del Dg
     if w.out_dtype == "f32":
         assert torch.isfinite(D).all()
     torch.cuda.synchronize()

@@ -22,6 +22,7 @@ def test_step_timeline(sched, group):
     D = empty_out(w)
     log("case timeline", sched, "group", group)
     with dg.Plan(w.M, w.N, w.K, w.L, w.TP, sched, w.dtype) as p:
+        p.set_option("EXECUTION", 0)
         p.set_option("STEP_GROUP", group)
         with pytest.raises(dg.DistGemmError):
             p.step_timeline()                       # nothing recorded yet
@@ -51,9 +52,34 @@ def test_step_timeline(sched, group):
     assert all(t > 0 for t in times)
 
 
+def test_single_launch_timeline():
+    """A single-launch run is one launch: every step reports its span, and no
+    separate copy completion (the copies are inside the launch)."""
+    import torch
+    import communication_tensor_gemm_amd as dg
+    w = workloads.small_case("tl_single", "AG_ROT_B", "BF16_F32", 1024, 1024, 256, 1, 8, 1.0, 0.0,
+                             seed=12)
+    x = workloads.generate(w)
+    A, B = to_gpu(x.A), to_gpu(x.B)
+    D = empty_out(w)
+    with dg.Plan(w.M, w.N, w.K, w.L, w.TP, w.schedule, w.dtype) as p:
+        p.set_option("EXECUTION", 1)
+        p.set_option("STEP_TIMING", 2)
+        for _ in range(3):
+            p.run(A, B, None, D, 1.0, 0.0)
+        torch.cuda.synchronize()
+        tl = p.step_timeline()
+        times = p.step_times()
+    check_full(w, x, D)
+    assert len({(b, e) for _, b, e in tl}) == 1
+    assert all(c == -1.0 and 0.0 <= b <= e for c, b, e in tl)
+    assert len(times) == 2 * w.TP and all(t > 0 for t in times)
+
+
+@pytest.mark.parametrize("execution", [0, 1])
 @pytest.mark.parametrize("sched,dtype", [("AG_ROT_A", "BF16_F32"), ("RS_TILE_A_ROT_C", "BF16_F32"),
                                          ("AG_ROT_B", "E4M3_BF16")])
-def test_graph_capture_replay(sched, dtype):
+def test_graph_capture_replay(sched, dtype, execution):
     """The run is capturable: one capture of dist_gemm_run on a side stream,
     replayed three times with eager work between the replays; every replay
     equals the eager run bit for bit."""
@@ -70,6 +96,7 @@ def test_graph_capture_replay(sched, dtype):
     with dg.Plan(w.M, w.N, w.K, w.L, w.TP, sched, w.dtype) as p:
         if w.in_dtype == "e4m3":
             p.set_scales(x.scale_a, x.scale_b)
+        p.set_option("EXECUTION", execution)
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
             p.run(A, B, C if beta else None, D_eager, w.alpha, beta, stream=s.cuda_stream)
