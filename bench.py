@@ -194,7 +194,7 @@ def main():
                     help="0 = step launches + side-stream copies, 1 = one persistent launch per run")
     ap.add_argument("--queues", type=int, default=8, help="work queues of the single launch (1 or 8)")
     ap.add_argument("--copy-chunk", type=int, default=2 << 20, help="bytes per copy item of the single launch")
-    ap.add_argument("--copy-ahead", type=int, default=2, help="copy lookahead of the single launch (groups)")
+    ap.add_argument("--copy-ahead", type=int, default=4, help="copy lookahead of the single launch (groups)")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")

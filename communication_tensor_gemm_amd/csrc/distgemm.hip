@@ -203,7 +203,7 @@ struct dist_gemm_plan_s {
   int32_t* d_sync = nullptr;
   uint64_t fused_align = 0;   // OR of the chunk widths (copy unit choice)
   int fused_groups = 0;       // launch groups in the device tables
-  int copy_ahead = 2;         // copy lookahead, launch groups
+  int copy_ahead = 4;         // copy lookahead, launch groups
   std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
   int compute_streams = 2;
@@ -794,8 +794,8 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       return rc;
     }
     case DIST_GEMM_OPT_COPY_AHEAD: {
-      if (value < 1 || value > 1024)
-        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy lookahead must be 1..1024");
+      if (value < 1 || value > 64)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy lookahead must be 1..64");
       if (plan->copy_ahead == value) return DIST_GEMM_OK;
       const int old_a = plan->copy_ahead;
       plan->copy_ahead = static_cast<int>(value);

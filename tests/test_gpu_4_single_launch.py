@@ -93,12 +93,13 @@ def test_single_launch_edges(M, N, K, TP, sched, dtype):
     assert torch.equal(D, run_plan(w, x, options={"EXECUTION": 0}))
 
 
-@pytest.mark.parametrize("queues,chunk,group", [(8, 4096, 2), (1, 4096, 1), (1, 1 << 20, 3),
-                                                (8, 16384, 1), (8, 1 << 28, 7), (8, 1 << 21, 1024)])
-def test_single_launch_queues_chunks_groups(queues, chunk, group):
+@pytest.mark.parametrize("queues,chunk,group,ahead", [(8, 4096, 2, 2), (1, 4096, 1, 1), (1, 1 << 20, 3, 2),
+                                                      (8, 16384, 1, 64), (8, 1 << 28, 7, 1),
+                                                      (8, 1 << 21, 1024, 3), (8, 4096, 1, 7)])
+def test_single_launch_queues_chunks_groups(queues, chunk, group, ahead):
     """Work distribution does not change a bit of the result: one queue or
-    one per XCD, chunks from 4 KiB (thousands of copy items) to one per shard,
-    launch groups from one step to all staged steps."""
+    one per XCD, chunks from 4 KiB (thousands of chunks) to one per shard,
+    launch groups from one step to all staged steps, copy lookahead 1 to all."""
     import torch
     for sched in ("AG_ROT_A", "AG_ROT_B", "RS_TILE_B_ROT_C"):
         w = workloads.small_case(f"fused_q{queues}_c{chunk}_g{group}_{sched}", sched, "BF16_F32", 1024,
@@ -106,9 +107,10 @@ def test_single_launch_queues_chunks_groups(queues, chunk, group):
         x = workloads.generate(w)
         log("case", w.name)
         D, nerr = _errors_after(w, x, {"EXECUTION": 1, "QUEUES": queues, "COPY_CHUNK": chunk,
-                                       "STEP_GROUP": group})
+                                       "STEP_GROUP": group, "COPY_AHEAD": ahead})
         assert nerr == 0
-        assert torch.equal(D, run_plan(w, x, options={"EXECUTION": 0})), (queues, chunk, group, sched)
+        assert torch.equal(D, run_plan(w, x, options={"EXECUTION": 0})), (queues, chunk, group, ahead,
+                                                                          sched)
 
 
 def test_single_launch_in_place_reduce_scatter():
@@ -235,7 +237,8 @@ def test_single_launch_option_errors():
     import communication_tensor_gemm_amd as dg
     with dg.Plan(512, 512, 64, 1, 2, "AG_ROT_A", "BF16_F32") as p:
         for opt, bad in (("EXECUTION", 2), ("QUEUES", 4), ("COPY_CHUNK", 4095), ("COPY_CHUNK", 4104),
-                         ("COPY_CHUNK", (1 << 28) + 16), ("WAIT_LIMIT_US", -1)):
+                         ("COPY_CHUNK", (1 << 28) + 16), ("WAIT_LIMIT_US", -1), ("COPY_AHEAD", 0),
+                         ("COPY_AHEAD", 65)):
             with pytest.raises(dg.DistGemmError):
                 p.set_option(opt, bad)
     # plans without staged steps accept the options and run step launches
