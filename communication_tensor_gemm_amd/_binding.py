@@ -19,7 +19,7 @@ SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_
 DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4}
 OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2, "COPY_STREAMS": 3,
            "STEP_GROUP": 4, "EXECUTION": 5, "QUEUES": 6, "COPY_CHUNK": 7, "WAIT_LIMIT_US": 8,
-           "COPY_AHEAD": 9}
+           "COPY_AHEAD": 9, "SHARED_A": 10}
 # bytes per element of (A/B, C/D) for each dtype
 ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
               "E4M3_F32": (1, 4)}
@@ -186,6 +186,7 @@ class Plan:
     def __init__(self, M, N, K, L=1, TP=1, schedule="MONOLITHIC", dtype="BF16_F32"):
         self.M, self.N, self.K, self.L, self.TP = M, N, K, L, TP
         self.schedule, self.dtype = schedule, dtype
+        self.shared_a = False
         self.handle = dist_gemm_plan(M, N, K, L, TP, schedule, dtype)
 
     def set_scales(self, scale_a, scale_b):
@@ -193,6 +194,8 @@ class Plan:
 
     def set_option(self, option, value):
         dist_gemm_set_option(self.handle, option, value)
+        if _enum(OPTIONS, option) == OPTIONS["SHARED_A"]:
+            self.shared_a = bool(value)
 
     def steps(self):
         return dist_gemm_plan_steps(self.handle)
@@ -219,7 +222,7 @@ class Plan:
     def run(self, A, B, C, D, alpha=1.0, beta=0.0, stream=None):
         ei, eo = ELEM_BYTES[self.dtype]
         M, N, K, L = self.M, self.N, self.K, self.L
-        self._need(A, L * M * K * ei, "A")
+        self._need(A, (1 if self.shared_a else L) * M * K * ei, "A")
         self._need(B, L * N * K * ei, "B")
         self._need(D, L * M * N * eo, "D")
         if C is not None:

@@ -42,6 +42,7 @@ struct Problem {
   int schedule = 0, dtype = 0;
   int in_kind = 0, out_kind = 0;
   int es_in = 0, es_out = 0;
+  bool shared_a = false;  // one A (M x K) for all L batches
 };
 
 int fail(std::string* where, int code, const std::string& msg) {
@@ -143,9 +144,9 @@ CopyGeom copy_geom(const Problem& p) {
   CopyGeom g;
   const size_t S = static_cast<size_t>(p.S);
   switch (p.schedule) {
-    case DIST_GEMM_AG_ROT_A:  // A row shard, per batch contiguous
+    case DIST_GEMM_AG_ROT_A:  // A row shard, per batch contiguous (one batch if A is shared)
       g.width = static_cast<size_t>(p.M / S) * p.K * p.es_in;
-      g.height = p.L;
+      g.height = p.shared_a ? 1 : p.L;
       g.src_pitch = static_cast<size_t>(p.M) * p.K * p.es_in;
       break;
     case DIST_GEMM_AG_ROT_B:  // B column shard = rows of the N x K storage
@@ -404,13 +405,14 @@ StepLayout step_layout(const dist_gemm_plan_s* P, const dist_gemm_step& st) {
   y.M = static_cast<int32_t>(st.m1 - st.m0);
   y.N = static_cast<int32_t>(st.n1 - st.n0);
   // defaults: operands in place
-  y.offA = st.m0 * K * ei;  y.lda = K; y.sA = M * K;
+  y.offA = st.m0 * K * ei;  y.lda = K; y.sA = pr.shared_a ? 0 : M * K;
   y.offB = st.n0 * K * ei;  y.ldb = K; y.sB = N * K;
   y.offC = (st.m0 * N + st.n0) * eo; y.ldc = N; y.sC = M * N;
   y.offD = (st.m0 * N + st.n0) * eo; y.ldd = N; y.sD = M * N;
   if (st.staged) {
     switch (pr.schedule) {
-      case DIST_GEMM_AG_ROT_A: y.stagedA = true; y.offA = slot; y.sA = slots * (M / S) * K; break;
+      case DIST_GEMM_AG_ROT_A:
+        y.stagedA = true; y.offA = slot; y.sA = pr.shared_a ? 0 : slots * (M / S) * K; break;
       case DIST_GEMM_AG_ROT_B: y.stagedB = true; y.offB = slot; y.sB = slots * (N / S) * K; break;
       case DIST_GEMM_RS_TILE_A_ROT_C:
         y.stagedC = true; y.offC = slot; y.ldc = N; y.sC = slots * (M / S) * N; break;
@@ -805,6 +807,24 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       const int rc = build_fused(plan, &plan->err);
       if (rc != DIST_GEMM_OK) {
         plan->copy_ahead = old_a;
+        (void)build_fused(plan, nullptr);
+      }
+      return rc;
+    }
+    case DIST_GEMM_OPT_SHARED_A: {
+      if (value != 0 && value != 1)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "shared A must be 0 or 1");
+      if (plan->pr.shared_a == (value != 0)) return DIST_GEMM_OK;
+      DeviceGuard guard(plan->device);
+      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+      // the staging buffer was sized for L batches: a shared A needs one
+      plan->pr.shared_a = value != 0;
+      plan->geom = copy_geom(plan->pr);
+      if (!plan->d_steps) return DIST_GEMM_OK;
+      const int rc = build_fused(plan, &plan->err);
+      if (rc != DIST_GEMM_OK) {
+        plan->pr.shared_a = !plan->pr.shared_a;
+        plan->geom = copy_geom(plan->pr);
         (void)build_fused(plan, nullptr);
       }
       return rc;

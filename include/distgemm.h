@@ -188,9 +188,15 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
  *     In correct operation no wait runs out.
  *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 1..64; the chunks of launch
  *     group h are carried by the tiles of group max(0, h - D), i.e. D
- *     groups ahead of their use; default 4 (measured: 0.5-2% faster than 2
- *     on the TP=8 workloads, where it puts every copy on the first group).  Larger D suits copy-bound
- *     workloads (partials much larger than the step's arithmetic). */
+ *     groups ahead of their use; default 4 (measured 0.5-2% faster than 2
+ *     on the TP=8 workloads, where it puts every copy on the first group).
+ *   DIST_GEMM_OPT_SHARED_A: 1 = A holds one M x K matrix that every one of
+ *     the L batches multiplies (B, C, D keep their L batches): the several-B
+ *     form of the PyTorch symmetric-memory page's fused all-gather matmul
+ *     (one gathered A, one output per B, e.g. the gate and up projections).
+ *     With AG_ROT_A the A shards are rotated once for all L products.
+ *     0 (default) = A has L batches like the other operands.  Waits for the
+ *     plan's last run when it changes. */
 enum dist_gemm_option {
   DIST_GEMM_OPT_COMPUTE_STREAMS = 0,
   DIST_GEMM_OPT_COPY_ENGINE = 1,
@@ -201,7 +207,8 @@ enum dist_gemm_option {
   DIST_GEMM_OPT_QUEUES = 6,
   DIST_GEMM_OPT_COPY_CHUNK = 7,
   DIST_GEMM_OPT_WAIT_LIMIT_US = 8,
-  DIST_GEMM_OPT_COPY_AHEAD = 9
+  DIST_GEMM_OPT_COPY_AHEAD = 9,
+  DIST_GEMM_OPT_SHARED_A = 10
 };
 int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
 
