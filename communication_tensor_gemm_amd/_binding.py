@@ -26,7 +26,7 @@ ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM", -5: "HIP"}
 
 # C functions declared in include/distgemm.h (checked by the CPU tests)
-C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
+C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
                "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
                "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                "dist_gemm_destroy", "dist_gemm_last_error", "dist_gemm_status_string")
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
                                          ctypes.POINTER(Step), ctypes.POINTER(i32)]
     lib.dist_gemm_plan.argtypes = [i64, i64, i64, i64, i32, i32, i32, ctypes.POINTER(vp)]
     lib.dist_gemm_set_scales.argtypes = [vp, ctypes.c_float, ctypes.c_float]
+    lib.dist_gemm_set_bias.argtypes = [vp, vp]
     lib.dist_gemm_set_option.argtypes = [vp, i32, i64]
     lib.dist_gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     lib.dist_gemm_plan_steps.argtypes = [vp, ctypes.POINTER(Step), ctypes.POINTER(i32)]
@@ -75,7 +76,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_last_error.restype = ctypes.c_char_p
     lib.dist_gemm_status_string.argtypes = [i32]
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
-    for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales",
+    for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
                  "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
                  "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                  "dist_gemm_destroy"):
@@ -115,6 +116,10 @@ def dist_gemm_plan(M, N, K, L, TP, schedule, dtype) -> ctypes.c_void_p:
 
 def dist_gemm_set_scales(plan, scale_a: float, scale_b: float):
     _check(lib.dist_gemm_set_scales(plan, scale_a, scale_b), plan)
+
+
+def dist_gemm_set_bias(plan, bias):
+    _check(lib.dist_gemm_set_bias(plan, _ptr(bias)), plan)
 
 
 def dist_gemm_set_option(plan, option, value: int):
@@ -191,6 +196,14 @@ class Plan:
 
     def set_scales(self, scale_a, scale_b):
         dist_gemm_set_scales(self.handle, scale_a, scale_b)
+
+    def set_bias(self, bias):
+        """bias: a GPU tensor of N output elements (fp32, or bf16 bits), or None.
+        The plan keeps its address; keep the tensor alive while runs may use it."""
+        if bias is not None and not isinstance(bias, int):
+            self._need(bias, self.N * ELEM_BYTES[self.dtype][1], "bias")
+        self._bias = bias
+        dist_gemm_set_bias(self.handle, bias)
 
     def set_option(self, option, value):
         dist_gemm_set_option(self.handle, option, value)

@@ -207,6 +207,7 @@ struct dist_gemm_plan_s {
   int copy_ahead = 4;         // copy lookahead, launch groups
   std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
+  const void* bias = nullptr;  // device, N values of the output type, or NULL
   int compute_streams = 2;
   int copy_engine = 2;  // library streaming copy kernel
   int copy_streams = 2;
@@ -388,7 +389,7 @@ std::vector<LaunchGroup> group_steps(const dist_gemm_plan_s* P) {
 // or (staged*) from the staging buffer, with leading dimensions and batch
 // strides in elements.
 struct StepLayout {
-  int64_t offA, offB, offC, offD;
+  int64_t offA, offB, offC, offD, offBias;
   int64_t lda, ldb, ldc, ldd, sA, sB, sC, sD;
   int32_t M, N;
   bool stagedA, stagedB, stagedC;
@@ -409,6 +410,7 @@ StepLayout step_layout(const dist_gemm_plan_s* P, const dist_gemm_step& st) {
   y.offB = st.n0 * K * ei;  y.ldb = K; y.sB = N * K;
   y.offC = (st.m0 * N + st.n0) * eo; y.ldc = N; y.sC = M * N;
   y.offD = (st.m0 * N + st.n0) * eo; y.ldd = N; y.sD = M * N;
+  y.offBias = st.n0 * eo;
   if (st.staged) {
     switch (pr.schedule) {
       case DIST_GEMM_AG_ROT_A:
@@ -441,6 +443,7 @@ dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, 
   g.C = (beta == 0.0f || (!y.stagedC && !C)) ? nullptr
                                              : (y.stagedC ? stg : static_cast<const uint8_t*>(C)) + y.offC;
   g.D = static_cast<uint8_t*>(D) + y.offD;
+  g.bias = P->bias ? static_cast<const uint8_t*>(P->bias) + y.offBias : nullptr;
   g.lda = y.lda; g.ldb = y.ldb; g.ldc = y.ldc; g.ldd = y.ldd;
   g.sA = y.sA; g.sB = y.sB; g.sC = y.sC; g.sD = y.sD;
   return g;
@@ -482,7 +485,7 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
     const dist_gemm_step& last = P->steps[grp.first + grp.count - 1];
     const StepLayout y = step_layout(P, st);
     dg::FusedStep& f = fs[gi];
-    f.offA = y.offA; f.offB = y.offB; f.offC = y.offC; f.offD = y.offD;
+    f.offA = y.offA; f.offB = y.offB; f.offC = y.offC; f.offD = y.offD; f.offBias = y.offBias;
     f.lda = y.lda; f.ldb = y.ldb; f.ldc = y.ldc; f.ldd = y.ldd;
     f.sA = y.sA; f.sB = y.sB; f.sC = y.sC; f.sD = y.sD;
     f.M = static_cast<int32_t>(std::max(st.m1, last.m1) - st.m0);
@@ -573,6 +576,7 @@ int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B,
   const CopyGeom& g = P->geom;
   dg::FusedArgs a{};
   a.A = A; a.B = B; a.C = beta != 0.0f ? C : nullptr; a.D = D;
+  a.bias = P->bias;
   a.staging = P->staging;
   a.copy_src = copy_src;
   a.steps = P->d_steps;
@@ -722,6 +726,12 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b) {
     return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "scales must be finite");
   plan->scale_a = scale_a;
   plan->scale_b = scale_b;
+  return DIST_GEMM_OK;
+}
+
+int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias) {
+  if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
+  plan->bias = bias;
   return DIST_GEMM_OK;
 }
 

@@ -139,6 +139,7 @@ __device__ __forceinline__ GemmParams fused_step_params(const FusedArgs& a, cons
   g.B = (st.stagedB ? stg : static_cast<const uint8_t*>(a.B)) + st.offB;
   g.C = a.beta != 0.0f ? (st.stagedC ? stg : static_cast<const uint8_t*>(a.C)) + st.offC : nullptr;
   g.D = static_cast<uint8_t*>(a.D) + st.offD;
+  g.bias = a.bias ? static_cast<const uint8_t*>(a.bias) + st.offBias : nullptr;
   g.lda = st.lda; g.ldb = st.ldb; g.ldc = st.ldc; g.ldd = st.ldd;
   g.sA = st.sA; g.sB = st.sB; g.sC = st.sC; g.sD = st.sD;
   g.M = st.M; g.N = st.N; g.K = a.K; g.L = a.L;

@@ -10,7 +10,7 @@ enum InKind { IN_F32 = 0, IN_BF16 = 1, IN_E4M3 = 2 };
 enum OutKind { OUT_F32 = 0, OUT_BF16 = 1 };
 
 // One GEMM over an (M x N) block of D, full K:
-//   D[i][j] = alpha * sum_k A[i][k] * B[j][k] + beta * C[i][j]
+//   D[i][j] = alpha * sum_k A[i][k] * B[j][k] + beta * C[i][j] (+ bias[j])
 // A rows are lda apart, B rows (the N index) ldb apart, both K-contiguous.
 // Strides and leading dimensions are in elements of the operand's type.
 struct GemmParams {
@@ -18,6 +18,7 @@ struct GemmParams {
   const void* B;
   const void* C;  // read only when beta != 0
   void* D;
+  const void* bias;  // NULL, or the block's first column of a bias vector (output type)
   int64_t lda, ldb, ldc, ldd;
   int64_t sA, sB, sC, sD;  // batch strides
   int32_t M, N, K, L;
@@ -53,6 +54,7 @@ struct FusedStep {
   int64_t offA, offB, offC, offD;  // bytes from the operand base (A / B / C / D or staging)
   int64_t lda, ldb, ldc, ldd;      // elements
   int64_t sA, sB, sC, sD;          // batch strides, elements
+  int64_t offBias;                 // bytes: the group's first column in the bias vector
   int64_t copy_src_off;            // bytes: the group's first shard in the rotating operand
   int64_t copy_dst_off;            // bytes: its staging slot
   int64_t chunk_cols, chunk_rows;
@@ -78,6 +80,7 @@ struct FusedArgs {
   const void* B;
   const void* C;           // NULL when beta == 0 (unless it is the rotating operand)
   void* D;
+  const void* bias;        // NULL or N values of the output type
   uint8_t* staging;
   const void* copy_src;    // the rotating operand (A, B or C)
   const FusedStep* steps;  // [S] launch groups

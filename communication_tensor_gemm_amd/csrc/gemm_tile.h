@@ -360,8 +360,15 @@ __device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int k
 template <typename M, int OUT>
 __device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc (&acc)[M::NB][M::NB],
                                                 const GemmParams& p, uint8_t* Dw, const uint8_t* Cw,
-                                                int rows_left, int cols_left) {
+                                                const uint8_t* Bw, int rows_left, int cols_left) {
   constexpr int OES = OUT == OUT_F32 ? 4 : 2;
+  // the lane's bias values, one per column block (Bw: the wave's first column)
+  float bv[M::NB];
+#pragma unroll
+  for (int j = 0; j < M::NB; ++j) {
+    const int col = M::out_col(j, lane);
+    bv[j] = (Bw && col < cols_left) ? load_out<OUT>(Bw, col) : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < M::NB; ++i) {
 #pragma unroll
@@ -376,6 +383,7 @@ __device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc 
         if (col < cols_left) {
           float v = p.alpha * acc[i][j][r];
           if (crow) v = __builtin_fmaf(p.beta, load_out<OUT>(crow, col), v);
+          if (Bw) v += bv[j];
           store_out<OUT>(drow, col, v);
         }
       }
@@ -398,7 +406,20 @@ template <typename M>
 __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lane,
                                                 const typename M::Acc (&acc)[M::NB][M::NB],
                                                 const GemmParams& p, uint8_t* Dw, const uint8_t* Cw,
-                                                int rows_left, int cols_left) {
+                                                const uint8_t* Bw, int rows_left, int cols_left) {
+  // the lane's four bias values (its columns are the same in every row)
+  const int bc = 4 * (lane & 31);
+  f32x4 bb = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (Bw) {
+    const float* bf = reinterpret_cast<const float*>(Bw);
+    if (bc + 4 <= cols_left) {
+      bb = *reinterpret_cast<const f32x4*>(bf + bc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (bc + e < cols_left) bb[e] = bf[bc + e];
+    }
+  }
   barrier_only();
   float* lds = reinterpret_cast<float*>(smem) + wave * kEpiWave;
   constexpr int kBlocksPerQuarter = 32 / M::BLK;
@@ -430,6 +451,7 @@ __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lan
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, c[e], v[e]);
           }
+          if (Bw) v += bb;
           *reinterpret_cast<f32x4*>(drow + cc) = v;
         } else {
 #pragma unroll
@@ -437,6 +459,7 @@ __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lan
             if (cc + e < cols_left) {
               float v = p.alpha * a[e];
               if (crow) v = __builtin_fmaf(p.beta, crow[cc + e], v);
+              if (Bw) v += bb[e];
               drow[cc + e] = v;
             }
         }
@@ -567,8 +590,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
 #pragma unroll
     for (int j = 0; j < M::NB; ++j) asm volatile("" : "+a"(acc[i][j]));
 
-  // Epilogue: D = alpha * acc + beta * C.  For fp32 output with D (and C)
-  // rows 16-byte aligned, each 32-row quarter of the wave's block goes through
+  // Epilogue: D = alpha * acc + beta * C (+ bias).  For fp32 output with D
+  // (and C, bias) rows 16-byte aligned, each 32-row quarter of the wave's block goes through
   // LDS so that every lane stores 16 contiguous bytes; otherwise element by
   // element.
   constexpr int OES = OUT == OUT_F32 ? 4 : 2;
@@ -576,11 +599,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   const uint8_t* Dl = static_cast<const uint8_t*>(p.D) + l * p.sD * OES;
   const uint8_t* Cl = use_c ? static_cast<const uint8_t*>(p.C) + l * p.sC * OES : nullptr;
   [[maybe_unused]] const uint64_t align = reinterpret_cast<uint64_t>(Dl) | static_cast<uint64_t>(p.ldd * OES) |
-                         (use_c ? reinterpret_cast<uint64_t>(Cl) | static_cast<uint64_t>(p.ldc * OES) : 0);
+                         (use_c ? reinterpret_cast<uint64_t>(Cl) | static_cast<uint64_t>(p.ldc * OES) : 0) |
+                         reinterpret_cast<uint64_t>(p.bias);
   const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
   const int rows_left = p.M - wrow0, cols_left = p.N - wcol0;
   uint8_t* Dw = const_cast<uint8_t*>(Dl) + (static_cast<int64_t>(wrow0) * p.ldd + wcol0) * OES;
   const uint8_t* Cw = use_c ? Cl + (static_cast<int64_t>(wrow0) * p.ldc + wcol0) * OES : nullptr;
+  const uint8_t* Bw = p.bias ? static_cast<const uint8_t*>(p.bias) + static_cast<int64_t>(wcol0) * OES : nullptr;
   // lane index redefined here, so that the epilogue's per-lane address
   // arithmetic is not hoisted above the main loop (where it would hold VGPRs
   // the fragment buffers need)
@@ -589,11 +614,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   // the condition is uniform over the workgroup (the barrier inside needs that)
   if constexpr (OUT == OUT_F32) {
     if ((align & 15) == 0) {
-      epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, rows_left, cols_left);
+      epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
       return;
     }
   }
-  epilogue_direct<M, OUT>(elane, acc, p, Dw, Cw, rows_left, cols_left);
+  epilogue_direct<M, OUT>(elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
 }
 
 template <int IN, int OUT>

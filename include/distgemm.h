@@ -126,6 +126,17 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
  * Returns INVALID_ARG for a NULL plan or non-finite scales. */
 int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
 
+/* Bias of the scaled matmul (the `bias` argument of _scaled_mm in the op
+ * schemas of the PyTorch symmetric-memory page): runs after this call compute
+ *   D = alpha*scale_a*scale_b*(A B) + beta*C + bias[j]
+ * for every row i and batch of column j.  `bias` is a device pointer to N
+ * values of the output element type (fp32 or bf16), read by every later run
+ * of the plan, so it must stay allocated while those runs may execute; the
+ * plan does not own it.  NULL (the default) removes the bias.  16-byte
+ * alignment keeps the vectorised fp32 epilogue; any alignment of the
+ * element is accepted.  Returns INVALID_ARG for a NULL plan. */
+int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
+
 /* Tuning options (host state of the plan; take effect at the next run).
  * Returns INVALID_ARG for a NULL plan, an unknown option or a value out of
  * range; the plan is unchanged then.

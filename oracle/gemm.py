@@ -1,4 +1,4 @@
-"""The step-scheduled fp64 GEMM  D = alpha * (sa*A) * (sb*B) + beta * C.
+"""The step-scheduled fp64 GEMM  D = alpha * (sa*A) * (sb*B) + beta * C (+ bias).
 
 Definition followed: the CUTLASS Distributed GEMM pages compare the
 distributed result against a single-device GEMM with the epilogue scalars
@@ -6,7 +6,8 @@ alpha (default 1) and beta (default 0) (example page, "Getting started"); the
 PyTorch symmetric-memory page defines the fused all-gather matmul as
 all_gather then matmul, the fused matmul reduce-scatter as matmul then
 reduce_scatter, and the scaled variants as _scaled_mm with per-tensor
-scale_a / scale_b (the op schemas and their fallbacks).
+scale_a / scale_b and an optional bias added to every row of the product
+(the op schemas and their fallbacks).
 
 The oracle walks the same step table as the GPU path: one numpy float64
 matmul per step on that step's row or column block, the epilogue in fp64,
@@ -14,7 +15,9 @@ written into that block.  Rounding to the output element happens once, at the
 end, in ``round_output``.
 
 Operand layout: A is L x M x K, B is stored L x N x K (the logical K x N
-operand with K contiguous), C and D are L x M x N.
+operand with K contiguous), C and D are L x M x N; the optional bias is one
+vector of N values in the output element type, the same for every row and
+batch.
 """
 from __future__ import annotations
 
@@ -39,11 +42,16 @@ def _as3(x):
     return None if x is None else (x if x.ndim == 3 else x[None])
 
 
+def _bias(bias, out_elem: str):
+    return None if bias is None else codecs.decode(np.asarray(bias).reshape(-1), out_elem)
+
+
 def dist_gemm(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem: str,
               out_elem: str, scale_a: float = 1.0, scale_b: float = 1.0,
-              rank: int = 0) -> np.ndarray:
+              rank: int = 0, bias=None) -> np.ndarray:
     """Unrounded fp64 D* of the whole schedule, shape L x M x N."""
     Ah, Bh, Ch = decode_operands(_as3(A), _as3(B), _as3(C), in_elem, out_elem, scale_a, scale_b)
+    bh = _bias(bias, out_elem)
     L, M, K = Ah.shape
     N = Bh.shape[1]
     if beta != 0.0 and Ch is None:
@@ -57,6 +65,8 @@ def dist_gemm(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem
             blk = np.float64(alpha) * acc
             if beta != 0.0:                                 # C is not read when beta == 0
                 blk = blk + np.float64(beta) * Ch[l, st.m0:st.m1, st.n0:st.n1]
+            if bh is not None:                              # bias: one value per column
+                blk = blk + bh[st.n0:st.n1][None, :]
             D[l, st.m0:st.m1, st.n0:st.n1] = blk
     return D
 
@@ -64,7 +74,7 @@ def dist_gemm(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem
 def dist_gemm_sampled(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem: str,
                       out_elem: str, rows: Sequence[int], cols: Sequence[int],
                       scale_a: float = 1.0, scale_b: float = 1.0, batch: int = 0,
-                      rank: int = 0):
+                      rank: int = 0, bias=None):
     """D* on the sub-grid rows x cols of batch `batch`, visiting the same steps.
 
     Only the sampled rows of A and columns of B are decoded, so this runs at
@@ -80,6 +90,7 @@ def dist_gemm_sampled(A, B, C, alpha: float, beta: float, schedule: str, S: int,
     c = None
     if beta != 0.0:
         c = codecs.decode(C3[batch][np.ix_(rows, cols)], out_elem)
+    bh = None if bias is None else _bias(bias, out_elem)[cols]
     D = np.full((len(rows), len(cols)), np.nan, dtype=np.float64)
     for st in step_table(schedule, M, N, S, rank):
         ri = np.nonzero((rows >= st.m0) & (rows < st.m1))[0]
@@ -90,6 +101,8 @@ def dist_gemm_sampled(A, B, C, alpha: float, beta: float, schedule: str, S: int,
         blk = np.float64(alpha) * acc
         if beta != 0.0:
             blk = blk + np.float64(beta) * c[np.ix_(ri, ci)]
+        if bh is not None:
+            blk = blk + bh[ci][None, :]
         D[np.ix_(ri, ci)] = blk
     return D, np.linalg.norm(a, axis=1), np.linalg.norm(b, axis=1)
 
@@ -99,12 +112,14 @@ def round_output(D: np.ndarray, out_elem: str) -> np.ndarray:
 
 
 def gemm_unchunked(A, B, C, alpha: float, beta: float, in_elem: str, out_elem: str,
-                   scale_a: float = 1.0, scale_b: float = 1.0) -> np.ndarray:
+                   scale_a: float = 1.0, scale_b: float = 1.0, bias=None) -> np.ndarray:
     """The same definition evaluated as one fp64 matmul per batch, no steps."""
     Ah, Bh, Ch = decode_operands(_as3(A), _as3(B), _as3(C), in_elem, out_elem, scale_a, scale_b)
     D = np.float64(alpha) * np.matmul(Ah, np.transpose(Bh, (0, 2, 1)))
     if beta != 0.0:
         D = D + np.float64(beta) * Ch
+    if bias is not None:
+        D = D + _bias(bias, out_elem)[None, None, :]
     return D
 
 

@@ -1,6 +1,6 @@
 """Per-element error of a device result against the oracle.
 
-err_ij = |D~_ij - D*_ij| / ( |alpha| * ||Ahat_i,:||_2 * ||Bhat_:,j||_2 + |beta| * |C_ij| )
+err_ij = |D~_ij - D*_ij| / ( |alpha| * ||Ahat_i,:||_2 * ||Bhat_:,j||_2 + |beta| * |C_ij| + |bias_j| )
 
 D* is the unrounded fp64 oracle value and Ahat/Bhat the decoded, scaled
 operands.  The normaliser bounds |D*_ij| (Cauchy-Schwarz), so the error is
@@ -29,18 +29,21 @@ BARS = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
 TIGHT_ACCUM = {"f32": 1e-5, "bf16": 1e-5, "e4m3": 1e-4}
 
 
-def normaliser(row_norms, col_norms, alpha: float, beta: float, C=None):
+def normaliser(row_norms, col_norms, alpha: float, beta: float, C=None, bias=None):
+    """bias: the decoded bias values of the compared columns (or None)."""
     den = abs(alpha) * np.outer(row_norms, col_norms)
     if beta != 0.0 and C is not None:
         den = den + abs(beta) * np.abs(C)
+    if bias is not None:
+        den = den + np.abs(np.asarray(bias, dtype=np.float64))[None, :]
     return den
 
 
 def normalised_error(D_dev, D_star, row_norms, col_norms, alpha: float, beta: float, C=None,
-                     out_elem: str = "f32"):
+                     out_elem: str = "f32", bias=None):
     """Returns the per-element error array (inf where it fails outright)."""
     D_dev = np.asarray(D_dev, dtype=np.float64)
-    den = normaliser(row_norms, col_norms, alpha, beta, C)
+    den = normaliser(row_norms, col_norms, alpha, beta, C, bias)
     diff = np.abs(D_dev - D_star)
     err = np.zeros_like(diff)
     pos = den > 0
@@ -53,13 +56,14 @@ def normalised_error(D_dev, D_star, row_norms, col_norms, alpha: float, beta: fl
     return err
 
 
-def check(D_dev, D_star, row_norms, col_norms, alpha, beta, C, in_elem: str, out_elem: str):
+def check(D_dev, D_star, row_norms, col_norms, alpha, beta, C, in_elem: str, out_elem: str,
+          bias=None):
     """(ok, max_err, tight_ok, detail) under the bar of the input element and the
-    tight output-rounding bar."""
-    err = normalised_error(D_dev, D_star, row_norms, col_norms, alpha, beta, C, out_elem)
+    tight output-rounding bar.  bias: decoded bias of the compared columns."""
+    err = normalised_error(D_dev, D_star, row_norms, col_norms, alpha, beta, C, out_elem, bias)
     mx = float(err.max()) if err.size else 0.0
     ok = mx <= BARS[in_elem]
-    den = normaliser(row_norms, col_norms, alpha, beta, C)
+    den = normaliser(row_norms, col_norms, alpha, beta, C, bias)
     diff = np.abs(np.asarray(D_dev, dtype=np.float64) - D_star)
     t = TIGHT_ACCUM[in_elem]
     if out_elem == "f32":

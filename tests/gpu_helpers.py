@@ -65,15 +65,17 @@ def run_plan(w: workloads.Workload, x: workloads.Inputs, schedule=None, TP=None,
     return D
 
 
-def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None):
-    """Element-by-element comparison with the full oracle.  Returns max err."""
+def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None, bias=None):
+    """Element-by-element comparison with the full oracle.  Returns max err.
+    bias: the bias bytes (N output elements) the run used, or None."""
     schedule = schedule or w.schedule
     TP = w.TP if TP is None else TP
     alpha = w.alpha if alpha is None else alpha
     beta = w.beta if beta is None else beta
     Dstar = gemm.dist_gemm(x.A, x.B, x.C if beta != 0 else None, alpha, beta, schedule,
                            TP if schedule != "MONOLITHIC" else 1, w.in_dtype, w.out_dtype,
-                           x.scale_a, x.scale_b)
+                           x.scale_a, x.scale_b, bias=bias)
+    bdec = None if bias is None else codecs.decode(np.asarray(bias).reshape(-1), w.out_dtype)
     got = from_gpu_out(D, w.out_dtype)
     worst = 0.0
     for l in range(w.L):
@@ -82,7 +84,7 @@ def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None):
         c = None if beta == 0 else codecs.decode(x.C[l], w.out_dtype)
         ok, mx, tight, _ = parity.check(got[l], Dstar[l], np.linalg.norm(a, axis=1),
                                         np.linalg.norm(b, axis=1), alpha, beta, c,
-                                        w.in_dtype, w.out_dtype)
+                                        w.in_dtype, w.out_dtype, bdec)
         assert ok, f"{w.name} batch {l}: max normalised error {mx}"
         assert tight, f"{w.name} batch {l}: tight bar failed (max err {mx})"
         worst = max(worst, mx)
@@ -104,12 +106,13 @@ def sample_indices(extent, steps, per_step, seed, tile=256):
     return np.array(sorted(i for i in idx if 0 <= i < extent), dtype=np.int64)
 
 
-def check_sampled(w, x, D, rows, cols, schedule=None, TP=None):
+def check_sampled(w, x, D, rows, cols, schedule=None, TP=None, bias=None):
     schedule = schedule or w.schedule
     TP = w.TP if TP is None else TP
     Dstar, rn, cn = gemm.dist_gemm_sampled(x.A, x.B, x.C, w.alpha, w.beta, schedule, TP,
                                            w.in_dtype, w.out_dtype, rows, cols, x.scale_a,
-                                           x.scale_b)
+                                           x.scale_b, bias=bias)
+    bdec = None if bias is None else codecs.decode(np.asarray(bias).reshape(-1), w.out_dtype)[cols]
     import torch
     ri = torch.from_numpy(rows).cuda()
     ci = torch.from_numpy(cols).cuda()
@@ -119,7 +122,7 @@ def check_sampled(w, x, D, rows, cols, schedule=None, TP=None):
     if w.beta != 0:
         c = codecs.decode(x.C[0][np.ix_(rows, cols)], w.out_dtype)
     ok, mx, tight, _ = parity.check(got, Dstar, rn, cn, w.alpha, w.beta, c, w.in_dtype,
-                                    w.out_dtype)
+                                    w.out_dtype, bdec)
     assert ok, f"{w.name}: sampled max normalised error {mx}"
     assert tight, f"{w.name}: sampled tight bar failed (max err {mx})"
     return mx

@@ -73,6 +73,7 @@ def test_validation_errors(args, status):
 
 def test_null_handles_are_rejected_without_gpu():
     assert dg.lib.dist_gemm_set_scales(None, 1.0, 1.0) == -1
+    assert dg.lib.dist_gemm_set_bias(None, None) == -1
     assert dg.lib.dist_gemm_set_option(None, 0, 1) == -1
     assert dg.lib.dist_gemm_run(None, None, None, None, None, 1.0, 0.0, None) == -1
     assert dg.lib.dist_gemm_destroy(None) == 0

@@ -224,3 +224,65 @@ def test_sampled_matches_full():
                                            rows, cols, batch=1)
         assert np.allclose(D, full[1][np.ix_(rows, cols)], rtol=1e-13, atol=1e-15)
         assert np.allclose(rn, np.linalg.norm(_torch_decode(x.A, "bf16")[1][rows], axis=1))
+
+
+def _bias_bytes(N, out_elem, seed):
+    """A bias vector in the output element's storage (float32, or bf16 bits)."""
+    v = np.random.default_rng(seed).standard_normal(N).astype(np.float32)
+    if out_elem == "f32":
+        return v
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["F32", "BF16_F32", "BF16_BF16", "E4M3_BF16"])
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_brute_force_exact_with_bias(dtype, sched):
+    """The scaled-matmul bias: one value per output column, added to every row
+    and batch; exact rational arithmetic, bias decoded by PyTorch."""
+    in_elem, out_elem = workloads.DTYPES[dtype]
+    for (M, N, K) in [(2, 3, 1), (4, 8, 3), (8, 4, 16)]:
+        for S in (1, 2, 4):
+            ext = M if sched in ("AG_ROT_A", "RS_TILE_A_ROT_C") else N
+            if sched != "MONOLITHIC" and ext % S:
+                continue
+            w, x = _inputs(dtype, M, N, K, L=2)
+            bias = _bias_bytes(N, out_elem, seed=M * 100 + N)
+            D = gemm.dist_gemm(x.A, x.B, x.C, w.alpha, w.beta, sched, S, in_elem, out_elem,
+                               x.scale_a, x.scale_b, bias=bias)
+            ex, mag = _brute(x.A, x.B, x.C, w.alpha, w.beta, in_elem, out_elem, x.scale_a,
+                             x.scale_b)
+            bt = _torch_decode(bias, out_elem)
+            bound = (K + 5) * 2.0 ** -53 * (mag + np.abs(bt)[None, None, :]) * 1.01
+            for idx in np.ndindex(D.shape):
+                exact = ex[idx] + Fraction(float(bt[idx[2]]))
+                err = abs(Fraction(float(D[idx])) - exact)
+                assert err <= Fraction(float(bound[idx])), (sched, dtype, M, N, K, S, idx)
+
+
+def test_bias_alone_and_linearity():
+    """alpha = beta = 0 leaves exactly the bias in every row; adding a bias
+    shifts every column of D by exactly that value (bias and D in fp64)."""
+    w, x = _inputs("BF16_BF16", 24, 40, 16, L=2)
+    bias = _bias_bytes(40, "bf16", seed=9)
+    bt = _torch_decode(bias, "bf16")
+    for sched in SCHEDS:
+        S = 4 if sched != "MONOLITHIC" else 1
+        D0 = gemm.dist_gemm(x.A, x.B, x.C, 0.0, 0.0, sched, S, "bf16", "bf16", bias=bias)
+        assert np.array_equal(D0, np.broadcast_to(bt, D0.shape))
+        Dn = gemm.dist_gemm(x.A, x.B, x.C, 1.5, 0.5, sched, S, "bf16", "bf16")
+        Db = gemm.dist_gemm(x.A, x.B, x.C, 1.5, 0.5, sched, S, "bf16", "bf16", bias=bias)
+        assert np.allclose(Db - Dn, np.broadcast_to(bt, Dn.shape), rtol=0, atol=1e-12)
+        un = gemm.gemm_unchunked(x.A, x.B, x.C, 1.5, 0.5, "bf16", "bf16", bias=bias)
+        assert np.allclose(Db, un, rtol=1e-13, atol=1e-13)
+
+
+def test_sampled_matches_full_with_bias():
+    w, x = _inputs("BF16_F32", 64, 48, 40, L=2)
+    bias = _bias_bytes(48, "f32", seed=4)
+    for sched in SCHEDS[:4]:
+        full = gemm.dist_gemm(x.A, x.B, x.C, w.alpha, w.beta, sched, 4, "bf16", "f32", bias=bias)
+        rows = [0, 5, 17, 63, 31]
+        cols = [47, 0, 12, 13]
+        D, rn, cn = gemm.dist_gemm_sampled(x.A, x.B, x.C, w.alpha, w.beta, sched, 4, "bf16", "f32",
+                                           rows, cols, batch=1, bias=bias)
+        assert np.allclose(D, full[1][np.ix_(rows, cols)], rtol=1e-13, atol=1e-15)

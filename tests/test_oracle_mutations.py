@@ -2,7 +2,8 @@
 
 Each case plants one plausible mistake in a temporary copy of the oracle
 (a dropped term, a transposed or reversed operand, a wrong scale, a wrong
-rotation or staging rule, a wrong exponent, double rounding) and runs the
+rotation or staging rule, a dropped or misindexed bias, a wrong exponent,
+double rounding) and runs the
 oracle's pin tests against that copy: every mutation must make them fail.
 """
 import os
@@ -22,6 +23,9 @@ MUTATIONS = [
     ("oracle/gemm.py", "blk = np.float64(alpha) * acc\n", "blk = np.float64(alpha) * acc * (1 + 2.0 ** -40)\n"),
     ("oracle/schedule.py", "j = (rank + s) % S ", "j = (rank + s + 1) % S "),
     ("oracle/schedule.py", "out.append(Step(s, j, lo, hi, 0, N, s > 0))", "out.append(Step(s, j, lo, hi, 0, N, s > 1))"),
+    ("oracle/gemm.py", "blk = blk + bh[st.n0:st.n1][None, :]", "blk = blk"),
+    ("oracle/gemm.py", "blk = blk + bh[st.n0:st.n1][None, :]", "blk = blk + bh[st.n0:st.n1][::-1][None, :]"),
+    ("oracle/gemm.py", "blk = blk + bh[ci][None, :]", "blk = blk + bh[ri % len(bh)][:, None]"),
     ("oracle/codecs.py", "t[code] = s * (m / 8.0) * 2.0 ** (1 - 7)", "t[code] = s * (m / 8.0) * 2.0 ** (0 - 7)"),
     ("oracle/codecs.py", "e = np.maximum(e - 1, emin)", "e = np.maximum(e, emin)"),
     ("oracle/codecs.py", "r = _round_to_grid(x, 7, -126)", "r = _round_to_grid(np.asarray(x, dtype=np.float32).astype(np.float64), 7, -126)"),
