@@ -4,7 +4,7 @@
  * The library computes, on one GPU, that GPU's share of a tensor-parallel
  * GEMM
  *
- *     D = alpha * (scale_a * A) * (scale_b * B) + beta * C
+ *     D = alpha * (scale_a * A) * (scale_b * B) + beta * C  (+ bias)
  *
  * as the sequence of TP steps that one of the Distributed GEMM schedules
  * prescribes (CUTLASS Distributed GEMM example page, "Trying out other
@@ -15,8 +15,13 @@
  * engine while the GEMM of the previous step runs, and each step's GEMM
  * waits for its operand before it starts.  On one GPU the peer's shard is a
  * region of the caller's full operand; the library copies it device to
- * device (SDMA, no compute units) into a plan-owned staging slot on a side
- * stream, and the step GEMM reads it from there.
+ * device into a plan-owned staging slot, and the step GEMM reads it from
+ * there.  By default one persistent kernel per run does both: its
+ * workgroups copy the shards in chunks ahead of use and compute the step
+ * tiles, each staged step's tiles starting once a device-side counter shows
+ * the step's shard complete (DIST_GEMM_OPT_EXECUTION = 1).  The alternative
+ * (= 0) launches the step GEMMs separately and copies on side streams,
+ * ordered by events.
  *
  * Layouts (all row-major, element strides, batch index outermost):
  *   A : L x M x K   (K contiguous, lda = K, batch stride M*K)
@@ -33,6 +38,9 @@
  * except where noted, and records a message readable with
  * dist_gemm_last_error(plan) (or dist_gemm_last_error(NULL) when there is
  * no plan).  The library never exits or aborts the process.
+ *
+ * Threads: calls on one plan must not run concurrently; different plans may
+ * be used from different host threads.
  */
 #ifndef DISTGEMM_H_
 #define DISTGEMM_H_
