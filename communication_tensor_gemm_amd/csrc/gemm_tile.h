@@ -193,6 +193,8 @@ struct Mma16Base {
   }
   // MFMA 16 x 16 result: lane holds column lane%16, rows 4*(lane/16) + r
   __device__ __forceinline__ static int out_row(int i, int r, int lane) { return 16 * i + 4 * (lane >> 4) + r; }
+  // 16-row part of the wave block that holds result register r of block row i
+  static constexpr int part_of(int i, int r) { return i; }
   __device__ __forceinline__ static int out_col(int j, int lane) { return 16 * j + (lane & 15); }
 };
 
@@ -253,6 +255,8 @@ struct Mma32Base {
   __device__ __forceinline__ static int out_row(int i, int r, int lane) {
     return 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
   }
+  // 16-row part of the wave block that holds result register r of block row i
+  static constexpr int part_of(int i, int r) { return 2 * i + (r >> 3); }
   __device__ __forceinline__ static int out_col(int j, int lane) { return 32 * j + (lane & 31); }
 };
 
@@ -399,8 +403,134 @@ __device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc 
 // output the element-wise stores are kept: the staged form measured equal for
 // bf16 inputs and 17% slower for e4m3 inputs.  The LDS ring is free by now; the
 // barrier makes sure no wave still reads it.
+//
+// C (beta != 0) of a wave block with all 128 x 128 elements in range is read
+// one quarter ahead into a second register buffer: the 16 loads of quarter
+// q + 1 are in flight while quarter q goes through LDS and is stored, so the
+// C reads of a tile overlap one another instead of costing one memory round
+// trip per 16 bytes.  Blocks at the edge of D keep the checked path.
 constexpr int kEpiRow = 128 + 4;             // floats per staged row (padded)
 constexpr int kEpiWave = 32 * kEpiRow;       // floats per wave: 16.5 KiB
+
+// The lane's 16 C vectors of quarter q: rows 32q + 2t + lane/32, columns
+// 4*(lane%32) .. +3 of the wave block.
+__device__ __forceinline__ void load_c_quarter(const float* Cf, int64_t ldc, int lane, int q,
+                                               f32x4 (&cq)[16]) {
+  const float* c0 = Cf + static_cast<int64_t>(32 * q + (lane >> 5)) * ldc + 4 * (lane & 31);
+#pragma unroll
+  for (int t = 0; t < 16; ++t) cq[t] = *reinterpret_cast<const f32x4*>(c0 + 2 * t * ldc);
+}
+
+// Full 128 x 128 wave block without C: no bounds checks.
+template <typename M>
+__device__ __forceinline__ void epilogue_staged_full(float* lds, int lane,
+                                                     const typename M::Acc (&acc)[M::NB][M::NB],
+                                                     const GemmParams& p, uint8_t* Dw, bool has_bias,
+                                                     f32x4 bb) {
+  constexpr int kBlocksPerQuarter = 32 / M::BLK;
+  const int bc = 4 * (lane & 31);
+  barrier_only();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int ib = 0; ib < kBlocksPerQuarter; ++ib) {
+      const int i = q * kBlocksPerQuarter + ib;
+#pragma unroll
+      for (int r = 0; r < M::R; ++r)
+#pragma unroll
+        for (int j = 0; j < M::NB; ++j)
+          lds[(M::out_row(i, r, lane) - 32 * q) * kEpiRow + M::out_col(j, lane)] = acc[i][j][r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // 32 lanes per row, 4 floats each; two rows per instruction
+    float* d0 = reinterpret_cast<float*>(Dw) + static_cast<int64_t>(32 * q + (lane >> 5)) * p.ldd + bc;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&lds[(2 * t + (lane >> 5)) * kEpiRow + bc]);
+      f32x4 v = a * p.alpha;
+      if (has_bias) v += bb;
+      *reinterpret_cast<f32x4*>(d0 + 2 * t * p.ldd) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
+  }
+}
+
+// Full 128 x 128 wave block with C (fp32), in eight parts of 16 rows.  The
+// C rows of part p + 1 go from memory straight into LDS (buffer_load ...
+// lds: 8 instructions per wave, each two 512-byte rows; lane l receives the
+// 16 bytes of row 2t + l/32, columns 4 (l % 32) ..) while part p is formed:
+// alpha * acc staged in the MFMA layout (16 x 132 floats per wave) and read
+// back by rows, and the lane adds beta times the very C bytes it loaded.  No
+// registers hold C (the persistent kernel has none to spare), C reads of
+// consecutive parts overlap, and only part 0 waits a full memory round trip.
+// LDS per wave: 8.25 KiB staging + two 8 KiB C buffers.
+constexpr int kEpiPartWave = 16 * kEpiRow * 4 + 2 * 8192;  // bytes
+// Every epilogue form places wave w's LDS area at w * kEpiWaveStride: the
+// waves of one workgroup may take different forms (a wave block past the
+// last row or column of D takes the checked one), and their areas must not
+// overlap.
+constexpr int kEpiWaveStride = kEpiPartWave > kEpiWave * 4 ? kEpiPartWave : kEpiWave * 4;
+static_assert(4 * kEpiWaveStride <= kSlots * kOperandSlab, "epilogue LDS");
+
+__device__ __forceinline__ void issue_c_part(const float* Cf, uint32_t ldc_b, int lane, int part,
+                                             uint8_t* buf) {
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(reinterpret_cast<const uint8_t*>(Cf) + static_cast<int64_t>(16 * part) * ldc_b, 16 * ldc_b);
+  const uint32_t off = static_cast<uint32_t>(lane >> 5) * ldc_b + 16 * (lane & 31);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(buf + 1024 * t), 16, off + 2 * t * ldc_b, 0, 0, 0);
+}
+
+template <typename M>
+__device__ __forceinline__ void epilogue_staged_c(uint8_t* smem, int wave, int lane,
+                                                  const typename M::Acc (&acc)[M::NB][M::NB],
+                                                  const GemmParams& p, uint8_t* Dw, const float* Cf,
+                                                  bool has_bias, f32x4 bb) {
+  const uint32_t ldc_b = static_cast<uint32_t>(p.ldc) * 4;
+  uint8_t* const base = smem + wave * kEpiWaveStride;
+  float* const stage = reinterpret_cast<float*>(base);
+  uint8_t* const cbuf[2] = {base + 16 * kEpiRow * 4, base + 16 * kEpiRow * 4 + 8192};
+  const int bc = 4 * (lane & 31);
+  barrier_only();  // no wave reads the operand ring any more
+  issue_c_part(Cf, ldc_b, lane, 0, cbuf[0]);
+#pragma unroll
+  for (int part = 0; part < 8; ++part) {
+    // wait for C of this part; C of the next part (issued now, 8 loads) and
+    // the stores of the previous part (8) may stay in flight
+    if (part < 7) {
+      issue_c_part(Cf, ldc_b, lane, part + 1, cbuf[(part + 1) & 1]);
+      if (part == 0)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < M::NB; ++i)
+#pragma unroll
+      for (int r = 0; r < M::R; ++r)
+        if (M::part_of(i, r) == part)
+#pragma unroll
+          for (int j = 0; j < M::NB; ++j)
+            stage[(M::out_row(i, r, lane) - 16 * part) * kEpiRow + M::out_col(j, lane)] = p.alpha * acc[i][j][r];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const uint8_t* const cb = cbuf[part & 1];
+    float* d0 = reinterpret_cast<float*>(Dw) + static_cast<int64_t>(16 * part + (lane >> 5)) * p.ldd + bc;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&stage[(2 * t + (lane >> 5)) * kEpiRow + bc]);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(cb + 1024 * t + 16 * lane);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, c[e], a[e]);
+      if (has_bias) v += bb;
+      *reinterpret_cast<f32x4*>(d0 + 2 * t * p.ldd) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffers are reused
+  }
+}
 
 template <typename M>
 __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lane,
@@ -419,9 +549,19 @@ __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lan
       for (int e = 0; e < 4; ++e)
         if (bc + e < cols_left) bb[e] = bf[bc + e];
     }
+    // complete the bias load here, so that no later wait counts it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  float* lds = reinterpret_cast<float*>(smem + wave * kEpiWaveStride);
+  // wave-uniform: the whole 128 x 128 block is inside D
+  if (rows_left >= 128 && cols_left >= 128 && p.ldc < (1 << 24)) {
+    if (Cw)
+      epilogue_staged_c<M>(smem, wave, lane, acc, p, Dw, reinterpret_cast<const float*>(Cw), Bw != nullptr, bb);
+    else
+      epilogue_staged_full<M>(lds, lane, acc, p, Dw, Bw != nullptr, bb);
+    return;
   }
   barrier_only();
-  float* lds = reinterpret_cast<float*>(smem) + wave * kEpiWave;
   constexpr int kBlocksPerQuarter = 32 / M::BLK;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
