@@ -151,9 +151,10 @@ template <int IN, int OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 fused_run_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * kOperandSlab];
-  // item broadcast word: in the last ring slot, which a tile first fills only
-  // after its prologue barrier (by then every wave has read the word)
-  volatile int32_t* bcast = reinterpret_cast<volatile int32_t*>(smem + (kSlots - 1) * kOperandSlab);
+  // item broadcast word: at the end of the last ring slot, which a tile first
+  // fills only after its prologue barrier (by then every wave has read the
+  // word) and which the epilogue leaves alone
+  volatile int32_t* bcast = reinterpret_cast<volatile int32_t*>(smem + kSlots * kOperandSlab - 256);
   const int tid = threadIdx.x;
   const int S = a.S;
   const int q = static_cast<int>(blockIdx.x) % a.nq;

@@ -456,21 +456,39 @@ __device__ __forceinline__ void epilogue_staged_full(float* lds, int lane,
 }
 
 // Full 128 x 128 wave block with C (fp32), in eight parts of 16 rows.  The
-// C rows of part p + 1 go from memory straight into LDS (buffer_load ...
+// C rows of part p + 2 go from memory straight into LDS (buffer_load ...
 // lds: 8 instructions per wave, each two 512-byte rows; lane l receives the
 // 16 bytes of row 2t + l/32, columns 4 (l % 32) ..) while part p is formed:
 // alpha * acc staged in the MFMA layout (16 x 132 floats per wave) and read
 // back by rows, and the lane adds beta times the very C bytes it loaded.  No
-// registers hold C (the persistent kernel has none to spare), C reads of
-// consecutive parts overlap, and only part 0 waits a full memory round trip.
-// LDS per wave: 8.25 KiB staging + two 8 KiB C buffers.
-constexpr int kEpiPartWave = 16 * kEpiRow * 4 + 2 * 8192;  // bytes
+// registers hold C (the persistent kernel has none to spare), and 16 KiB of
+// C per wave stay in flight, so the C reads of a tile overlap one another.
+// LDS per wave: 8.25 KiB staging + three 8 KiB C buffers.
+constexpr int kEpiCParts = 8;      // 16-row parts of a wave block
+constexpr int kEpiCAhead = 2;      // parts of C in flight ahead of the one in use
+constexpr int kEpiCBufs = kEpiCAhead + 1;
+constexpr int kEpiStage = 16 * kEpiRow * 4;  // bytes of staging per wave
+constexpr int kEpiPartWave = kEpiStage + kEpiCBufs * 8192;
 // Every epilogue form places wave w's LDS area at w * kEpiWaveStride: the
 // waves of one workgroup may take different forms (a wave block past the
 // last row or column of D takes the checked one), and their areas must not
-// overlap.
+// overlap.  The last 256 bytes of LDS stay free for the persistent kernel's
+// work-item broadcast.
 constexpr int kEpiWaveStride = kEpiPartWave > kEpiWave * 4 ? kEpiPartWave : kEpiWave * 4;
-static_assert(4 * kEpiWaveStride <= kSlots * kOperandSlab, "epilogue LDS");
+static_assert(4 * kEpiWaveStride <= kSlots * kOperandSlab - 256, "epilogue LDS");
+
+// Memory operations of one wave in the C epilogue, in issue order: C parts
+// 0 .. kEpiCAhead - 1, then for each part p the C load of part p +
+// kEpiCAhead (if any) followed, after the wait, by the 8 stores of part p.
+// epi_c_wait(p) = instructions issued after part p's C load when part p
+// waits for it (the s_waitcnt vmcnt immediate; loads and stores share the
+// counter and retire in order).
+constexpr int epi_c_wait(int p) {
+  int after = 0;
+  for (int c = p + 1; c < kEpiCParts && c <= p + kEpiCAhead; ++c) after += 8;  // later C loads
+  for (int d = p - kEpiCAhead > 0 ? p - kEpiCAhead : 0; d < p; ++d) after += 8;  // stores since
+  return after;
+}
 
 __device__ __forceinline__ void issue_c_part(const float* Cf, uint32_t ldc_b, int lane, int part,
                                              uint8_t* buf) {
@@ -482,6 +500,45 @@ __device__ __forceinline__ void issue_c_part(const float* Cf, uint32_t ldc_b, in
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(buf + 1024 * t), 16, off + 2 * t * ldc_b, 0, 0, 0);
 }
 
+template <typename M, int P>
+__device__ __forceinline__ void epilogue_c_part(uint8_t* base, int lane,
+                                                const typename M::Acc (&acc)[M::NB][M::NB],
+                                                const GemmParams& p, uint8_t* Dw, const float* Cf,
+                                                uint32_t ldc_b, bool has_bias, f32x4 bb) {
+  float* const stage = reinterpret_cast<float*>(base);
+  if constexpr (P + kEpiCAhead < kEpiCParts)
+    issue_c_part(Cf, ldc_b, lane, P + kEpiCAhead, base + kEpiStage + 8192 * ((P + kEpiCAhead) % kEpiCBufs));
+  wait_vmcnt<epi_c_wait(P)>();  // C of this part has landed
+#pragma unroll
+  for (int i = 0; i < M::NB; ++i)
+#pragma unroll
+    for (int r = 0; r < M::R; ++r)
+      if (M::part_of(i, r) == P)
+#pragma unroll
+        for (int j = 0; j < M::NB; ++j)
+          stage[(M::out_row(i, r, lane) - 16 * P) * kEpiRow + M::out_col(j, lane)] = p.alpha * acc[i][j][r];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint8_t* const cb = base + kEpiStage + 8192 * (P % kEpiCBufs);
+  const int bc = 4 * (lane & 31);
+  f32x4 a[8], c[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    a[t] = *reinterpret_cast<const f32x4*>(&stage[(2 * t + (lane >> 5)) * kEpiRow + bc]);
+    c[t] = *reinterpret_cast<const f32x4*>(cb + 1024 * t + 16 * lane);
+  }
+  float* d0 = reinterpret_cast<float*>(Dw) + static_cast<int64_t>(16 * P + (lane >> 5)) * p.ldd + bc;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, c[t][e], a[t][e]);
+    if (has_bias) v += bb;
+    *reinterpret_cast<f32x4*>(d0 + 2 * t * p.ldd) = v;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffers are reused
+  if constexpr (P + 1 < kEpiCParts) epilogue_c_part<M, P + 1>(base, lane, acc, p, Dw, Cf, ldc_b, has_bias, bb);
+}
+
 template <typename M>
 __device__ __forceinline__ void epilogue_staged_c(uint8_t* smem, int wave, int lane,
                                                   const typename M::Acc (&acc)[M::NB][M::NB],
@@ -489,47 +546,10 @@ __device__ __forceinline__ void epilogue_staged_c(uint8_t* smem, int wave, int l
                                                   bool has_bias, f32x4 bb) {
   const uint32_t ldc_b = static_cast<uint32_t>(p.ldc) * 4;
   uint8_t* const base = smem + wave * kEpiWaveStride;
-  float* const stage = reinterpret_cast<float*>(base);
-  uint8_t* const cbuf[2] = {base + 16 * kEpiRow * 4, base + 16 * kEpiRow * 4 + 8192};
-  const int bc = 4 * (lane & 31);
   barrier_only();  // no wave reads the operand ring any more
-  issue_c_part(Cf, ldc_b, lane, 0, cbuf[0]);
 #pragma unroll
-  for (int part = 0; part < 8; ++part) {
-    // wait for C of this part; C of the next part (issued now, 8 loads) and
-    // the stores of the previous part (8) may stay in flight
-    if (part < 7) {
-      issue_c_part(Cf, ldc_b, lane, part + 1, cbuf[(part + 1) & 1]);
-      if (part == 0)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    }
-#pragma unroll
-    for (int i = 0; i < M::NB; ++i)
-#pragma unroll
-      for (int r = 0; r < M::R; ++r)
-        if (M::part_of(i, r) == part)
-#pragma unroll
-          for (int j = 0; j < M::NB; ++j)
-            stage[(M::out_row(i, r, lane) - 16 * part) * kEpiRow + M::out_col(j, lane)] = p.alpha * acc[i][j][r];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const uint8_t* const cb = cbuf[part & 1];
-    float* d0 = reinterpret_cast<float*>(Dw) + static_cast<int64_t>(16 * part + (lane >> 5)) * p.ldd + bc;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(&stage[(2 * t + (lane >> 5)) * kEpiRow + bc]);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(cb + 1024 * t + 16 * lane);
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.beta, c[e], a[e]);
-      if (has_bias) v += bb;
-      *reinterpret_cast<f32x4*>(d0 + 2 * t * p.ldd) = v;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffers are reused
-  }
+  for (int c = 0; c < kEpiCAhead; ++c) issue_c_part(Cf, ldc_b, lane, c, base + kEpiStage + 8192 * c);
+  epilogue_c_part<M, 0>(base, lane, acc, p, Dw, Cf, ldc_b, has_bias, bb);
 }
 
 template <typename M>
