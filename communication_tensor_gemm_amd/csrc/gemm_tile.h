@@ -556,6 +556,63 @@ __device__ __forceinline__ void epilogue_staged_c(uint8_t* smem, int wave, int l
   epilogue_c_part<M, 0>(base, lane, acc, p, Dw, Cf, ldc_b, has_bias, bb);
 }
 
+// bf16 output without C, whole 128 x 128 wave block, D rows 8-byte aligned:
+// the same fp32 staging as above, read back 4 consecutive values per lane,
+// rounded to bf16 (RNE, as the element-wise form) and stored as 8 bytes, so
+// a wave writes two 256-byte row pieces per store instead of 2 bytes per lane.
+// Element-wise 2-byte stores measured about 5% of the e4m3 8192 x 13312 x
+// 16384 GEMM.  The caller has passed the workgroup barrier.
+template <typename M>
+__device__ __forceinline__ void epilogue_staged_bf16(uint8_t* smem, int wave, int lane,
+                                                     const typename M::Acc (&acc)[M::NB][M::NB],
+                                                     const GemmParams& p, uint8_t* Dw, const uint8_t* Bw) {
+  constexpr int kBlocksPerQuarter = 32 / M::BLK;
+  float* const lds = reinterpret_cast<float*>(smem + wave * kEpiWaveStride);
+  const int bc = 4 * (lane & 31);
+  // the lane's four bias values (its columns are the same in every row)
+  float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (Bw) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = load_out<OUT_BF16>(Bw, bc + e);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int ib = 0; ib < kBlocksPerQuarter; ++ib) {
+      const int i = q * kBlocksPerQuarter + ib;
+#pragma unroll
+      for (int r = 0; r < M::R; ++r)
+#pragma unroll
+        for (int j = 0; j < M::NB; ++j)
+          lds[(M::out_row(i, r, lane) - 32 * q) * kEpiRow + M::out_col(j, lane)] = acc[i][j][r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint16_t* d0 = reinterpret_cast<uint16_t*>(Dw) + static_cast<int64_t>(32 * q + (lane >> 5)) * p.ldd + bc;
+    // eight rows pairs at a time: their LDS reads are issued together
+#pragma unroll
+    for (int t0 = 0; t0 < 16; t0 += 8) {
+      f32x4 a[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        a[t] = *reinterpret_cast<const f32x4*>(&lds[(2 * (t0 + t) + (lane >> 5)) * kEpiRow + bc]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = p.alpha * a[t][e];
+          if (Bw) v += bv[e];
+          h[e] = f32_to_bf16_rne(v);
+        }
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+        const u32x2 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        *reinterpret_cast<u32x2*>(d0 + 2 * (t0 + t) * p.ldd) = w;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
+  }
+}
+
 template <typename M>
 __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lane,
                                                 const typename M::Acc (&acc)[M::NB][M::NB],
@@ -780,6 +837,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
     if ((align & 15) == 0) {
       epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
       return;
+    }
+  } else {
+    if ((align & 7) == 0 && !use_c) {
+      barrier_only();  // every wave is done with the operand ring (uniform branch)
+      if (rows_left >= 128 && cols_left >= 128) {
+        epilogue_staged_bf16<M>(smem, wave, elane, acc, p, Dw, Bw);
+        return;
+      }
     }
   }
   epilogue_direct<M, OUT>(elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
