@@ -141,8 +141,9 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
  * values of the output element type (fp32 or bf16), read by every later run
  * of the plan, so it must stay allocated while those runs may execute; the
  * plan does not own it.  NULL (the default) removes the bias.  16-byte
- * alignment keeps the vectorised fp32 epilogue; any alignment of the
- * element is accepted.  Returns INVALID_ARG for a NULL plan. */
+ * alignment (fp32 output) or 8-byte alignment (bf16 output) keeps the
+ * vectorised epilogue; any alignment of the element is accepted.  Returns
+ * INVALID_ARG for a NULL plan. */
 int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
 
 /* Tuning options (host state of the plan; take effect at the next run).
@@ -240,6 +241,10 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  *   allowed.  A and B are only read.
  * Buffers must stay allocated until the work completes on `stream`.  A run
  * on another stream first waits for the plan's previous run.
+ * Any element alignment is correct; D and C with 16-byte aligned base and
+ * row pitch (fp32 output), or D with 8-byte aligned base and row pitch (bf16
+ * output, beta == 0), take the vectorised epilogue, other layouts an
+ * element-wise one.
  * Errors: INVALID_ARG (NULL plan/A/B/D, C NULL with beta != 0, non-finite
  * alpha/beta); HIP if an enqueue fails (earlier steps may be enqueued).
  * Graph capture: with DIST_GEMM_OPT_STEP_TIMING = 0 and the plan's previous
