@@ -57,7 +57,91 @@ def to_gpu(arr):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
-def timed_runs(plan, args_run, steps, warmup, timing_runs):
+class SclkSampler:
+    """Shader clock read from the amdgpu sysfs level table (pp_dpm_sclk: the
+    current level is marked '*') every few milliseconds on a background
+    thread.  The reported level lags the load by a fraction of a second, so it
+    is sampled over a sustained phase of the same runs (see sustained_sclk),
+    not over the short timed region.  Unavailable (no readable table, or
+    several GPUs without a match for device 0) -> no samples."""
+
+    def __init__(self):
+        import glob
+        self.path = None
+        self.samples = []
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(paths) > 1:
+            try:
+                import torch
+                bus = str(getattr(torch.cuda.get_device_properties(0), "pci_bus_id", "")).lower()
+                paths = [q for q in paths if bus and bus in os.path.realpath(os.path.dirname(q)).lower()]
+            except Exception:
+                paths = []
+        if len(paths) == 1 and self._read(paths[0]) is not None:
+            self.path = paths[0]
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except Exception:
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+        self._t = None
+        if self.path:
+            def loop():
+                while not self._stop.is_set():
+                    v = self._read(self.path)
+                    if v is not None:
+                        self.samples.append(v)
+                    self._stop.wait(0.005)
+            self._t = threading.Thread(target=loop, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t:
+            self._t.join()
+        return False
+
+    def summary(self, skip_fraction=0.0):
+        v = self.samples[int(len(self.samples) * skip_fraction):]
+        if not v:
+            return None
+        v = sorted(v)
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                "source": "pp_dpm_sclk"}
+
+
+def sustained_sclk(plan, args_run, seconds=1.5):
+    """Run the plan back to back for about `seconds` and sample the shader
+    clock; the second half of the samples (after the reported level has
+    settled) is summarised.  None where the clock cannot be read."""
+    import torch
+    sampler = SclkSampler()
+    if not sampler.path:
+        return None
+    with sampler:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                plan.run(*args_run)
+            torch.cuda.synchronize()
+    out = sampler.summary(skip_fraction=0.5)
+    if out:
+        out["phase_s"] = seconds
+    return out
+
+
+def timed_runs(plan, args_run, steps, warmup, timing_runs, sampler=None):
     import torch
     for _ in range(warmup):
         plan.run(*args_run)
@@ -68,13 +152,15 @@ def timed_runs(plan, args_run, steps, warmup, timing_runs):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for b, e in evs:
-        b.record()
-        plan.run(*args_run)
-        e.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    import contextlib
+    with (sampler if sampler is not None else contextlib.nullcontext()):
+        t0 = time.perf_counter()
+        for b, e in evs:
+            b.record()
+            plan.run(*args_run)
+            e.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     step_ms = plan.step_times() if timing_runs else []
     run_ms = sorted(b.elapsed_time(e) for b, e in evs)
     stats = {"mean": sum(run_ms) / len(run_ms), "median": run_ms[len(run_ms) // 2], "min": run_ms[0]}
@@ -277,6 +363,7 @@ def main():
     parity = parity_spot_check(w, x, D)
     log(f"[bench] parity spot check: {parity}")
 
+
     mono = None
     if not args.no_mono:
         with dg.Plan(w.M, w.N, w.K, w.L, 1, "MONOLITHIC", w.dtype) as mp:
@@ -290,6 +377,11 @@ def main():
         log(f"[bench] monolithic {mono_ms:.3f} ms ({mono['tflops']:.1f} TFLOP/s); "
             f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
     wait_timeouts = plan.device_errors()
+    # after both timed comparisons, so that neither starts from a GPU this
+    # phase has warmed
+    plan.set_option("STEP_TIMING", 0)
+    sclk_stats = sustained_sclk(plan, run_args)
+    log(f"[bench] shader clock while the runs repeat: {sclk_stats}")
     plan.close()
     del A, B, C, D
     torch.cuda.empty_cache()
@@ -323,6 +415,11 @@ def main():
                    "queues": args.queues, "copy_chunk": args.copy_chunk,
                    "copy_ahead": args.copy_ahead},
         "pct_mfma_peak": round(100 * value / peak, 2),
+        # the same rate against the peak at the shader clock measured while
+        # the same runs execute back to back (the published peak assumes 2400 MHz)
+        "sclk_mhz": sclk_stats,
+        "pct_mfma_peak_at_sclk": (round(100 * value / (peak * sclk_stats["median"] / 2400.0), 2)
+                                  if sclk_stats else None),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": recorded_traffic(w.name),
