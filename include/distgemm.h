@@ -241,6 +241,10 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  *   allowed.  A and B are only read.
  * Buffers must stay allocated until the work completes on `stream`.  A run
  * on another stream first waits for the plan's previous run.
+ * A reduce-scatter that averages over the ranks (the reduce_op "avg" of the
+ * fused matmul + reduce-scatter on the PyTorch symmetric-memory page) is
+ * alpha = 1/TP: every rank scales its own contribution before the partials
+ * are summed, so each chunk's sum is the average.
  * Any element alignment is correct; D and C with 16-byte aligned base and
  * row pitch (fp32 output), or D with 8-byte aligned base and row pitch (bf16
  * output, beta == 0), take the vectorised epilogue, other layouts an
