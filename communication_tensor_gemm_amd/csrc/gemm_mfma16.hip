@@ -1,7 +1,6 @@
 // Instantiations of the tile GEMM for the 16 x 16 MFMA family (bf16 and
-// fp32 inputs), as per-step launches and as the single-launch run.  Built
-// with MFMA accumulators in VGPR form, which keeps this family's fragment
-// buffers out of scratch.
+// fp32 inputs), as per-step launches and as the single-launch run.  A unit
+// of its own because the fp32 half slab needs a higher unroll threshold.
 #include "fused_run.h"
 
 namespace dg {

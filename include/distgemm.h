@@ -242,9 +242,11 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  * Buffers must stay allocated until the work completes on `stream`.  A run
  * on another stream first waits for the plan's previous run.
  * A reduce-scatter that averages over the ranks (the reduce_op "avg" of the
- * fused matmul + reduce-scatter on the PyTorch symmetric-memory page) is
- * alpha = 1/TP: every rank scales its own contribution before the partials
- * are summed, so each chunk's sum is the average.
+ * fused matmul + reduce-scatter on the PyTorch symmetric-memory page, which
+ * averages the ranks' scaled-matmul outputs, bias included) is every rank
+ * scaling its whole contribution by 1/TP before the partials are summed:
+ * alpha = 1/TP and, with a bias, a bias vector divided by TP (the bias is
+ * added once per step, so the sum reduction passes it unscaled).
  * Any element alignment is correct; D and C with 16-byte aligned base and
  * row pitch (fp32 output), or D with 8-byte aligned base and row pitch (bf16
  * output, beta == 0), take the vectorised epilogue, other layouts an

@@ -286,3 +286,38 @@ def test_sampled_matches_full_with_bias():
         D, rn, cn = gemm.dist_gemm_sampled(x.A, x.B, x.C, w.alpha, w.beta, sched, 4, "bf16", "f32",
                                            rows, cols, batch=1, bias=bias)
         assert np.allclose(D, full[1][np.ix_(rows, cols)], rtol=1e-13, atol=1e-15)
+
+
+
+@pytest.mark.parametrize("sched", ["RS_TILE_A_ROT_C", "RS_TILE_B_ROT_C"])
+@pytest.mark.parametrize("op", ["avg", "sum"])
+def test_reduce_scatter_chain_with_bias(sched, op):
+    """The fused (scaled) matmul + reduce-scatter of the PyTorch
+    symmetric-memory page reduces the ranks' scaled-matmul outputs, each of
+    which includes the bias, with reduce_op sum or avg: the result is
+    sum_r (A_r B_r + bias) or its mean.  Read here as a chain of this GPU's
+    share over the TP ranks (beta = 1, each output the next rank's incoming
+    partial, starting from zero), where avg passes alpha = 1/TP and the bias
+    divided by TP.  The oracle chained that way must give the reduction
+    written out from its definition, up to the fp32 storage of the partials."""
+    TP, M, N, K = 4, 8, 12, 16
+    g = np.random.default_rng(21)
+    As = [g.standard_normal((1, M, K)).astype(np.float32) for _ in range(TP)]
+    Bs = [g.standard_normal((1, N, K)).astype(np.float32) for _ in range(TP)]
+    bias = g.standard_normal(N).astype(np.float32)
+    div = TP if op == "avg" else 1
+    part = np.zeros((1, M, N), dtype=np.float32)
+    for r in range(TP):
+        b = (bias.astype(np.float64) / div).astype(np.float32)
+        part = gemm.round_output(gemm.dist_gemm(As[r], Bs[r], part, 1.0 / div, 1.0, sched, TP,
+                                                "f32", "f32", rank=r, bias=b), "f32")
+    want = np.zeros((M, N))
+    for r in range(TP):
+        want += As[r][0].astype(np.float64) @ Bs[r][0].astype(np.float64).T + bias.astype(np.float64)
+    want /= div
+    mag = sum(np.abs(As[r][0]).astype(np.float64) @ np.abs(Bs[r][0]).astype(np.float64).T
+              + np.abs(bias) for r in range(TP)) / div
+    assert np.all(np.abs(part[0] - want) <= 4 * TP * 2.0 ** -24 * mag)
+    # and not the other reduction: avg and sum differ by a factor TP
+    other = want * TP if op == "avg" else want / TP
+    assert not np.allclose(part[0], other)

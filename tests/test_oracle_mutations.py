@@ -3,7 +3,7 @@
 Each case plants one plausible mistake in a temporary copy of the oracle
 (a dropped term, a transposed or reversed operand, a wrong scale, a wrong
 rotation or staging rule, a dropped or misindexed bias, a wrong exponent,
-double rounding) and runs the
+double rounding, a loosened or misindexed parity normaliser) and runs the
 oracle's pin tests against that copy: every mutation must make them fail.
 """
 import os
@@ -29,7 +29,23 @@ MUTATIONS = [
     ("oracle/codecs.py", "t[code] = s * (m / 8.0) * 2.0 ** (1 - 7)", "t[code] = s * (m / 8.0) * 2.0 ** (0 - 7)"),
     ("oracle/codecs.py", "e = np.maximum(e - 1, emin)", "e = np.maximum(e, emin)"),
     ("oracle/codecs.py", "r = _round_to_grid(x, 7, -126)", "r = _round_to_grid(np.asarray(x, dtype=np.float32).astype(np.float64), 7, -126)"),
+    # the parity metric's normaliser and bars
+    ("oracle/parity.py", "den = den + abs(beta) * np.abs(C)", "den = den + beta * np.abs(C)"),
+    ("oracle/parity.py", "den = den + abs(beta) * np.abs(C)", "den = den + 4 * abs(beta) * np.abs(C)"),
+    ("oracle/parity.py", "den = den + abs(beta) * np.abs(C)", "den = den"),
+    ("oracle/parity.py", "if beta != 0.0 and C is not None:", "if C is not None:"),
+    ("oracle/parity.py", "den = den + np.abs(np.asarray(bias, dtype=np.float64))[None, :]", "den = den"),
+    ("oracle/parity.py", "den = den + np.abs(np.asarray(bias, dtype=np.float64))[None, :]",
+     "den = den + 4 * np.abs(np.asarray(bias, dtype=np.float64))[None, :]"),
+    ("oracle/parity.py", "den = den + np.abs(np.asarray(bias, dtype=np.float64))[None, :]",
+     "den = den + np.abs(np.asarray(bias, dtype=np.float64))[:, None]"),
+    ("oracle/parity.py", "den = abs(alpha) * np.outer(row_norms, col_norms)", "den = alpha * np.outer(row_norms, col_norms)"),
+    ("oracle/parity.py", "tight = bool(np.all(diff <= 2.0 ** -8 * np.abs(D_star) + t * den))",
+     "tight = bool(np.all(diff <= 2.0 ** -7 * np.abs(D_star) + t * den))"),
 ]
+
+
+PIN_TESTS = ("test_oracle_codecs.py", "test_oracle_gemm.py", "test_oracle_parity_and_inputs.py")
 
 
 @pytest.mark.parametrize("idx", range(len(MUTATIONS)))
@@ -39,12 +55,12 @@ def test_pins_catch_planted_mistake(idx, tmp_path):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("__pycache__"))
     (tmp_path / "tests").mkdir()
-    for t in ("conftest.py", "test_oracle_codecs.py", "test_oracle_gemm.py"):
+    for t in PIN_TESTS + ("conftest.py",):
         shutil.copy(os.path.join(ROOT, "tests", t), tmp_path / "tests" / t)
     src = (tmp_path / f).read_text()
     assert old in src, f"mutation anchor not found in {f}"
     (tmp_path / f).write_text(src.replace(old, new, 1))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_codecs.py", "tests/test_oracle_gemm.py"],
+                        *[f"tests/{t}" for t in PIN_TESTS]],
                        cwd=tmp_path, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutation {idx}: {new!r}\n{r.stdout[-2000:]}"

@@ -76,3 +76,105 @@ def test_config_table():
     assert c3.flops == 2.0 * 16384 * 13312 * 16384
     assert c["c4_rs_tile_a_rot_c_bf16_tp8"].beta == 1.0
     assert c["c5_ag_rot_b_e4m3_tp8"].out_dtype == "bf16"
+
+
+# ---- the beta*|C|, |alpha| and |bias| terms of the normaliser ---------------
+#
+# Each case builds operands whose norms make one term dominate the
+# normaliser, plants one element error at a known multiple of the f32 bar
+# times the true normaliser of that element, and checks both sides of the
+# bar: 0.3 x bar must pass and 3 x bar must fail.  A dropped term shrinks
+# the normaliser (the 0.3 x case then fails), an inflated one grows it (the
+# 3 x case then passes), and a dropped abs() makes it non-positive for a
+# negative scalar (the 0.3 x case then needs an exact value and fails).
+
+def _true_den(rn, cn, alpha, beta, C, bias):
+    """The normaliser written out element by element from its definition."""
+    den = np.empty((len(rn), len(cn)))
+    for i in range(len(rn)):
+        for j in range(len(cn)):
+            v = abs(alpha) * rn[i] * cn[j]
+            if beta != 0.0:
+                v += abs(beta) * abs(C[i, j])
+            if bias is not None:
+                v += abs(bias[j])
+            den[i, j] = v
+    return den
+
+
+def _plant(alpha, beta, C, bias, rn, cn, factor, at=(2, 3)):
+    g = np.random.default_rng(11)
+    Dstar = g.standard_normal((len(rn), len(cn)))
+    den = _true_den(rn, cn, alpha, beta, C, bias)
+    dev = Dstar.copy()
+    dev[at] += factor * parity.BARS["f32"] * den[at]
+    return parity.check(dev, Dstar, rn, cn, alpha, beta, C, "f32", "f32", bias)
+
+
+@pytest.mark.parametrize("beta", [1.0, -0.5])
+def test_metric_c_term_scales_the_bar(beta):
+    # tiny operand norms: the normaliser is |beta| * |C| almost everywhere
+    rn = np.full(6, 1e-4)
+    cn = np.full(5, 1e-4)
+    C = np.random.default_rng(5).uniform(50.0, 100.0, (6, 5)) * np.where(
+        np.arange(30).reshape(6, 5) % 2 == 0, 1.0, -1.0)
+    ok, mx, _, _ = _plant(1.0, beta, C, None, rn, cn, 0.3)
+    assert ok and 0.25 * parity.BARS["f32"] < mx < 0.35 * parity.BARS["f32"]
+    ok, mx, _, _ = _plant(1.0, beta, C, None, rn, cn, 3.0)
+    assert not ok and 2.9 * parity.BARS["f32"] < mx < 3.1 * parity.BARS["f32"]
+
+
+def test_metric_c_term_ignored_when_beta_is_zero():
+    # beta = 0: C is not part of the result, so it must not loosen the bar
+    rn = np.full(6, 1e-4)
+    cn = np.full(5, 1e-4)
+    C = np.full((6, 5), 1e6)
+    ok, _, _, _ = _plant(1.0, 0.0, C, None, rn, cn, 3.0)
+    assert not ok
+    # nor can a non-finite C that is never read spoil a correct result
+    C[1, 1] = np.inf
+    C[2, 2] = np.nan
+    ok, mx, tight, _ = _plant(1.0, 0.0, C, None, rn, cn, 0.3)
+    assert ok and tight and np.isfinite(mx)
+
+
+@pytest.mark.parametrize("alpha", [2.0, -2.0])
+def test_metric_alpha_term_scales_the_bar(alpha):
+    rn = np.random.default_rng(6).uniform(1.0, 3.0, 6)
+    cn = np.random.default_rng(7).uniform(1.0, 3.0, 5)
+    assert _plant(alpha, 0.0, None, None, rn, cn, 0.3)[0]
+    assert not _plant(alpha, 0.0, None, None, rn, cn, 3.0)[0]
+
+
+def test_metric_bias_term_scales_the_bar():
+    rn = np.full(6, 1e-4)
+    cn = np.full(5, 1e-4)
+    bias = np.array([40.0, -60.0, 80.0, -90.0, 70.0])
+    for at in [(2, 3), (0, 1), (5, 4)]:
+        ok, mx, _, _ = _plant(1.0, 0.0, None, bias, rn, cn, 0.3, at)
+        assert ok and mx > 0.25 * parity.BARS["f32"]
+        assert not _plant(1.0, 0.0, None, bias, rn, cn, 3.0, at)[0]
+
+
+def test_metric_bias_and_c_terms_add():
+    rn = np.full(6, 1e-4)
+    cn = np.full(5, 1e-4)
+    C = np.full((6, 5), -30.0)
+    bias = np.full(5, 30.0)
+    # both terms count: 0.6 x the bar measured against |C| alone passes only
+    # because the bias term doubles the normaliser
+    ok, mx, _, _ = _plant(1.0, -1.0, C, bias, rn, cn, 0.3)
+    assert ok and 0.25 * parity.BARS["f32"] < mx < 0.35 * parity.BARS["f32"]
+    assert not _plant(1.0, -1.0, C, bias, rn, cn, 3.0)[0]
+
+
+def test_bf16_output_tight_bar_is_half_an_ulp_of_rounding():
+    # the tight bf16-output bar allows 2^-8 |D*| (round to nearest), not more
+    g = np.random.default_rng(4)
+    Dstar = g.uniform(1.0, 2.0, (32, 32)) * np.where(g.random((32, 32)) < 0.5, -1.0, 1.0)
+    rn = np.full(32, 1e-3)
+    dev = Dstar * (1 + 0.9 * 2.0 ** -8)
+    assert parity.check(dev, Dstar, rn, rn, 1.0, 0.0, None, "bf16", "bf16")[2]
+    dev = Dstar.copy()
+    dev[7, 9] = Dstar[7, 9] * (1 + 1.5 * 2.0 ** -8)
+    assert not parity.check(dev, Dstar, rn, rn, 1.0, 0.0, None, "bf16", "bf16")[2]
