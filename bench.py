@@ -31,6 +31,8 @@ METRIC = "TFLOP/s + % MFMA peak of TP-step GEMM at TP=8 shard shapes, 1 MI355X"
 # MI355X dense MFMA peaks (TFLOP/s) by input element type
 PEAK = {"bf16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
 DEFAULT_CONFIG = "c3_ag_rot_a_bf16_tp8"
+# the metric's other TP=8 shard shapes, timed in the same run as sub-records
+SUB_CONFIGS = ["c4_rs_tile_a_rot_c_bf16_tp8", "c5_ag_rot_b_e4m3_tp8"]
 
 
 def log(*a):
@@ -141,7 +143,7 @@ def sustained_sclk(plan, args_run, seconds=1.5):
     return out
 
 
-def timed_runs(plan, args_run, steps, warmup, timing_runs, sampler=None):
+def timed_runs(plan, args_run, steps, warmup, timing_runs, sampler=None, name="run"):
     import torch
     for _ in range(warmup):
         plan.run(*args_run)
@@ -156,9 +158,11 @@ def timed_runs(plan, args_run, steps, warmup, timing_runs, sampler=None):
     with (sampler if sampler is not None else contextlib.nullcontext()):
         t0 = time.perf_counter()
         for b, e in evs:
+            ROCTX.push(name)
             b.record()
             plan.run(*args_run)
             e.record()
+            ROCTX.pop()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     step_ms = plan.step_times() if timing_runs else []
@@ -265,6 +269,191 @@ def calibrate_copy(nbytes, reps):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+class Roctx:
+    """roctx ranges around every timed run (rocprofv3 --marker-trace shows
+    them), through the ROCm tracer library if it loads; otherwise a no-op."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        for name in ("libroctx64.so", "/opt/rocm/lib/libroctx64.so"):
+            try:
+                self.lib = ctypes.CDLL(name)
+                self.lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+                break
+            except OSError:
+                continue
+
+    def push(self, name: str):
+        if self.lib:
+            self.lib.roctxRangePushA(name.encode())
+
+    def pop(self):
+        if self.lib:
+            self.lib.roctxRangePop()
+
+
+ROCTX = Roctx()
+
+
+def make_plan(w, x, args, options=None):
+    import communication_tensor_gemm_amd as dg
+    plan = dg.Plan(w.M, w.N, w.K, w.L, w.TP, w.schedule, w.dtype)
+    if w.in_dtype == "e4m3":
+        plan.set_scales(x.scale_a, x.scale_b)
+    opts = {"COMPUTE_STREAMS": args.compute_streams, "COPY_ENGINE": args.copy_engine,
+            "COPY_STREAMS": args.copy_streams, "STEP_GROUP": args.step_group,
+            "EXECUTION": args.execution, "QUEUES": args.queues, "COPY_CHUNK": args.copy_chunk,
+            "COPY_AHEAD": args.copy_ahead}
+    opts.update(options or {})
+    for k, v in opts.items():
+        plan.set_option(k, v)
+    return plan
+
+
+def copy_alone_ms(w, A, B, C, reps=5):
+    """The rotation's bytes (the S-1 staged shards) moved by a plain device
+    copy on an otherwise idle GPU: what the copies cost when nothing runs
+    beside them."""
+    import torch
+    S = w.TP
+    if w.schedule == "AG_ROT_A":
+        src = A.view(w.L, S, -1)
+    elif w.schedule == "AG_ROT_B":
+        src = B.view(w.L, S, -1)
+    elif w.schedule == "RS_TILE_A_ROT_C":
+        src = C.view(w.L, S, -1)
+    else:
+        src = C.view(w.L * w.M, S, -1)
+    src = src[:, 1:]
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = b.elapsed_time(e) / reps
+    nbytes = src.numel() * src.element_size()
+    del dst
+    return {"ms": round(ms, 4), "bytes": nbytes, "GB_per_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "what": "the S-1 staged shards copied by a plain device copy (torch copy_), GPU otherwise idle"}
+
+
+def measure(w, args, headline):
+    """Time one workload: the schedule, its monolithic GEMM, parity, the
+    rotation's copy alone; the sustained clock for the headline only."""
+    import numpy as np
+    import torch
+
+    import workloads
+    S = w.TP if w.schedule != "MONOLITHIC" else 1
+    log(f"[bench] workload {w.name}: {w.schedule} {w.dtype} M={w.M} N={w.N} K={w.K} TP={w.TP}")
+    t = time.perf_counter()
+    x = workloads.generate(w)
+    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f}s")
+    A, B, C = to_gpu(x.A), to_gpu(x.B), to_gpu(x.C)
+    out_dt = torch.float32 if w.out_dtype == "f32" else torch.int16
+    D = torch.empty((w.L, w.M, w.N), dtype=out_dt, device="cuda")
+    plan = make_plan(w, x, args)
+    run_args = (A, B, C if w.beta != 0 else None, D, w.alpha, w.beta)
+    log(f"[bench] timing {args.steps} runs after {args.warmup} warmup runs")
+    fused = args.execution == 1 and S > 1
+    # One launch per run: the per-run events on the launch's stream time the
+    # launch itself, so the timed runs carry no per-step instrumentation;
+    # the step timeline comes from two more runs afterwards.
+    ms, step_ms, run_stats = timed_runs(plan, run_args, args.steps, args.warmup, not fused, name=w.name)
+    value = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK[w.in_dtype]
+    if fused:
+        _, _, _ = timed_runs(plan, run_args, 2, 0, True, name=w.name + ".timeline")
+    timeline = plan.step_timeline()
+    if fused:
+        n_launch = 1
+        avg_launch_ms = run_stats["mean"]
+        busy = avg_launch_ms
+    else:
+        # Steps merged into one launch share its duration equally; the time at
+        # least one step GEMM ran (overlapping launches on two compute streams
+        # stretch each one's span) comes from the last run's timeline.
+        spans = sorted({(b, e) for _, b, e in timeline})
+        busy, cur = 0.0, None
+        for b, e in spans:
+            if cur is None or b > cur[1]:
+                if cur is not None:
+                    busy += cur[1] - cur[0]
+                cur = [b, e]
+            else:
+                cur[1] = max(cur[1], e)
+        busy += cur[1] - cur[0]
+        n_launch = len(spans)
+        avg_launch_ms = float(np.mean(step_ms)) * S / n_launch
+    flops_per_launch = w.flops / n_launch
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    achieved_busy = w.flops / (busy * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/run, {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak); "
+        f"{n_launch} launches/run, per-launch {achieved:.1f} TFLOP/s")
+    parity = parity_spot_check(w, x, D)
+    log(f"[bench] parity spot check: {parity}")
+    mono = None
+    if not args.no_mono:
+        import communication_tensor_gemm_amd as dg
+        with dg.Plan(w.M, w.N, w.K, w.L, 1, "MONOLITHIC", w.dtype) as mp:
+            if w.in_dtype == "e4m3":
+                mp.set_scales(x.scale_a, x.scale_b)
+            mono_ms, mono_steps, mono_stats = timed_runs(mp, run_args, args.steps, args.warmup, True,
+                                                         name=w.name + ".monolithic")
+        mono = {"ms": round(mono_ms, 4), "tflops": round(w.flops / (mono_ms * 1e-3) / 1e12, 2),
+                "kernel_ms": round(float(np.mean(mono_steps)), 4),
+                "run_ms": {k: round(v, 4) for k, v in mono_stats.items()},
+                "exposed_overhead": round(ms / mono_ms - 1.0, 4)}
+        log(f"[bench] monolithic {mono_ms:.3f} ms ({mono['tflops']:.1f} TFLOP/s); "
+            f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
+    copy_alone = copy_alone_ms(w, A, B, C) if S > 1 else None
+    log(f"[bench] rotation copy alone: {copy_alone}")
+    wait_timeouts = plan.device_errors()
+    sclk_stats = None
+    if headline:
+        # after both timed comparisons, so that neither starts from a GPU
+        # this phase has warmed
+        plan.set_option("STEP_TIMING", 0)
+        sclk_stats = sustained_sclk(plan, run_args)
+        log(f"[bench] shader clock while the runs repeat: {sclk_stats}")
+    plan.close()
+    del A, B, C, D
+    torch.cuda.empty_cache()
+    rec = {
+        "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "config": {"workload": w.name, "schedule": w.schedule, "M": w.M, "N": w.N, "K": w.K,
+                   "L": w.L, "TP": w.TP, "in": w.in_dtype, "out": w.out_dtype,
+                   "alpha": w.alpha, "beta": w.beta},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(w.name),
+                     "kernel": ("gemm_tn_kernel (step GEMM launches)" if args.execution == 0 else
+                                "fused_run_kernel (one launch: shard copies and all tiles)"),
+                     "avg_launch_ms": round(avg_launch_ms, 4),
+                     "flops_per_launch": flops_per_launch, "launches_per_run": n_launch,
+                     "gemm_busy_ms": round(busy, 4),
+                     "achieved_while_busy": round(achieved_busy, 2)},
+        "timeline_last_run": {"copy_done_ms": [round(t[0], 4) for t in timeline],
+                              "gemm_begin_ms": [round(t[1], 4) for t in timeline],
+                              "gemm_end_ms": [round(t[2], 4) for t in timeline]},
+        "run_ms": {k: round(v, 4) for k, v in run_stats.items()},
+        "monolithic": mono,
+        # the single launch computes the monolithic tile grid, so without its
+        # copies it is the monolithic kernel: t_nocopy is its time
+        "t_nocopy_ms": mono["ms"] if (mono and args.execution == 1) else None,
+        "t_copy_only": copy_alone,
+        "parity": parity,
+        "device_wait_timeouts": wait_timeouts,
+    }
+    return rec, x, sclk_stats
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +474,8 @@ def main():
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-mono", action="store_true", help="skip the monolithic comparison")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="time only --config, not the other TP=8 workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run plain copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -299,92 +490,17 @@ def main():
               file=sys.stderr, flush=True)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
     import torch
-
-    import communication_tensor_gemm_amd as dg
-    import workloads
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     w = pick_config(args.config)
-    S = w.TP if w.schedule != "MONOLITHIC" else 1
-    log(f"[bench] workload {w.name}: {w.schedule} {w.dtype} M={w.M} N={w.N} K={w.K} TP={w.TP}")
-    t = time.perf_counter()
-    x = workloads.generate(w)
-    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f}s")
-    A, B, C = to_gpu(x.A), to_gpu(x.B), to_gpu(x.C)
-    out_dt = torch.float32 if w.out_dtype == "f32" else torch.int16
-    D = torch.empty((w.L, w.M, w.N), dtype=out_dt, device="cuda")
-
-    plan = dg.Plan(w.M, w.N, w.K, w.L, w.TP, w.schedule, w.dtype)
-    if w.in_dtype == "e4m3":
-        plan.set_scales(x.scale_a, x.scale_b)
-    plan.set_option("COMPUTE_STREAMS", args.compute_streams)
-    plan.set_option("COPY_ENGINE", args.copy_engine)
-    plan.set_option("COPY_STREAMS", args.copy_streams)
-    plan.set_option("STEP_GROUP", args.step_group)
-    plan.set_option("EXECUTION", args.execution)
-    plan.set_option("QUEUES", args.queues)
-    plan.set_option("COPY_CHUNK", args.copy_chunk)
-    plan.set_option("COPY_AHEAD", args.copy_ahead)
-    run_args = (A, B, C if w.beta != 0 else None, D, w.alpha, w.beta)
-    log(f"[bench] timing {args.steps} runs after {args.warmup} warmup runs")
-    ms, step_ms, run_stats = timed_runs(plan, run_args, args.steps, args.warmup, True)
-    value = w.flops / (ms * 1e-3) / 1e12
-    peak = PEAK[w.in_dtype]
-    # Steps merged into one launch share its duration equally, so the mean
-    # per-step time makes achieved = flops of all launches / their summed
-    # durations (the flops-weighted average launch).
-    launch_ms = float(np.mean(step_ms))
-    flops_per_step = w.flops / S
-    achieved = flops_per_step / (launch_ms * 1e-3) / 1e12
-    # Last timed run: launches, and the time at least one step GEMM ran
-    # (overlapping launches on two compute streams stretch each one's span).
-    timeline = plan.step_timeline()
-    spans = sorted({(b, e) for _, b, e in timeline})
-    busy, cur = 0.0, None
-    for b, e in spans:
-        if cur is None or b > cur[1]:
-            if cur is not None:
-                busy += cur[1] - cur[0]
-            cur = [b, e]
-        else:
-            cur[1] = max(cur[1], e)
-    busy += cur[1] - cur[0]
-    achieved_busy = w.flops / (busy * 1e-3) / 1e12
-    n_launch = len(spans)
-    avg_launch_ms = launch_ms * S / n_launch       # mean duration of one launch
-    flops_per_launch = w.flops / n_launch           # mean algorithmic flops of one launch
-    log(f"[bench] {ms:.3f} ms/run, {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak); "
-        f"{len(spans)} launches/run, per-launch {achieved:.1f} TFLOP/s, "
-        f"while a GEMM runs {achieved_busy:.1f} TFLOP/s")
-
-    parity = parity_spot_check(w, x, D)
-    log(f"[bench] parity spot check: {parity}")
-
-
-    mono = None
-    if not args.no_mono:
-        with dg.Plan(w.M, w.N, w.K, w.L, 1, "MONOLITHIC", w.dtype) as mp:
-            if w.in_dtype == "e4m3":
-                mp.set_scales(x.scale_a, x.scale_b)
-            mono_ms, mono_steps, mono_stats = timed_runs(mp, run_args, args.steps, args.warmup, True)
-        mono = {"ms": mono_ms, "tflops": w.flops / (mono_ms * 1e-3) / 1e12,
-                "kernel_ms": float(np.mean(mono_steps)),
-                "run_ms": {k: round(v, 4) for k, v in mono_stats.items()},
-                "exposed_overhead": ms / mono_ms - 1.0}
-        log(f"[bench] monolithic {mono_ms:.3f} ms ({mono['tflops']:.1f} TFLOP/s); "
-            f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
-    wait_timeouts = plan.device_errors()
-    # after both timed comparisons, so that neither starts from a GPU this
-    # phase has warmed
-    plan.set_option("STEP_TIMING", 0)
-    sclk_stats = sustained_sclk(plan, run_args)
-    log(f"[bench] shader clock while the runs repeat: {sclk_stats}")
-    plan.close()
-    del A, B, C, D
-    torch.cuda.empty_cache()
+    rec, x, sclk_stats = measure(w, args, headline=True)
+    subs = {}
+    if not args.no_sub:
+        for name in [n for n in SUB_CONFIGS if pick_config(n).name != w.name]:
+            sub, _, _ = measure(pick_config(name), args, headline=False)
+            subs[sub["config"]["workload"]] = sub
 
     cpu = None
     if not args.no_cpu:
@@ -393,52 +509,48 @@ def main():
         log(f"[bench] CPU oracle {cpu['value'] * 1e3:.1f} GFLOP/s in {cpu['seconds']:.1f}s")
 
     dtype_name = {"bf16": "bf16", "f32": "f32", "e4m3": "e4m3"}[w.in_dtype]
-    rec = {
+    peak = PEAK[w.in_dtype]
+    config = dict(rec["config"])
+    config.update({"compute_streams": args.compute_streams,
+                   "copy_engine": ["sdma", "runtime_device_copy", "copy_kernel"][args.copy_engine],
+                   "copy_streams": args.copy_streams, "step_group": args.step_group,
+                   "execution": ["step_launches", "single_launch"][args.execution],
+                   "queues": args.queues, "copy_chunk": args.copy_chunk,
+                   "copy_ahead": args.copy_ahead})
+    out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": rec["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype_name,
         "data": "synthetic",
-        "config": {"workload": w.name, "schedule": w.schedule, "M": w.M, "N": w.N, "K": w.K,
-                   "L": w.L, "TP": w.TP, "in": w.in_dtype, "out": w.out_dtype,
-                   "alpha": w.alpha, "beta": w.beta, "compute_streams": args.compute_streams,
-                   "copy_engine": ["sdma", "runtime_device_copy", "copy_kernel"][args.copy_engine],
-                   "copy_streams": args.copy_streams, "step_group": args.step_group,
-                   "execution": ["step_launches", "single_launch"][args.execution],
-                   "queues": args.queues, "copy_chunk": args.copy_chunk,
-                   "copy_ahead": args.copy_ahead},
-        "pct_mfma_peak": round(100 * value / peak, 2),
+        "config": config,
+        "pct_mfma_peak": rec["pct_mfma_peak"],
         # the same rate against the peak at the shader clock measured while
         # the same runs execute back to back (the published peak assumes 2400 MHz)
         "sclk_mhz": sclk_stats,
-        "pct_mfma_peak_at_sclk": (round(100 * value / (peak * sclk_stats["median"] / 2400.0), 2)
+        "pct_mfma_peak_at_sclk": (round(100 * rec["value"] / (peak * sclk_stats["median"] / 2400.0), 2)
                                   if sclk_stats else None),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(w.name),
-                     "kernel": ("gemm_tn_kernel (step GEMM launches)" if args.execution == 0 else
-                                "fused_run_kernel (one launch: shard copies and step GEMMs)"),
-                     "avg_launch_ms": round(avg_launch_ms, 4),
-                     "flops_per_launch": flops_per_launch, "launches_per_run": n_launch,
-                     "gemm_busy_ms": round(busy, 4),
-                     "achieved_while_busy": round(achieved_busy, 2)},
-        "timeline_last_run": {"copy_done_ms": [round(t[0], 4) for t in timeline],
-                              "gemm_begin_ms": [round(t[1], 4) for t in timeline],
-                              "gemm_end_ms": [round(t[2], 4) for t in timeline]},
-        "run_ms": {k: round(v, 4) for k, v in run_stats.items()},
-        "monolithic": mono,
-        "parity": parity,
-        "device_wait_timeouts": wait_timeouts,
+        "roofline": rec["roofline"],
+        "timeline_last_run": rec["timeline_last_run"],
+        "run_ms": rec["run_ms"],
+        "monolithic": rec["monolithic"],
+        "t_nocopy_ms": rec["t_nocopy_ms"],
+        "t_copy_only": rec["t_copy_only"],
+        "parity": rec["parity"],
+        "device_wait_timeouts": rec["device_wait_timeouts"],
         "cpu_baseline": cpu,
+        # the other TP=8 shard shapes of the metric, measured the same way in
+        # the same process (not part of value)
+        "other_workloads": subs,
     }
-    print(json.dumps(rec), flush=True)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

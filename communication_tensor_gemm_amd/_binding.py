@@ -19,7 +19,7 @@ SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_
 DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4}
 OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2, "COPY_STREAMS": 3,
            "STEP_GROUP": 4, "EXECUTION": 5, "QUEUES": 6, "COPY_CHUNK": 7, "WAIT_LIMIT_US": 8,
-           "COPY_AHEAD": 9, "SHARED_A": 10}
+           "COPY_AHEAD": 9, "SHARED_A": 10, "COPY_DELAY_US": 11}
 # bytes per element of (A/B, C/D) for each dtype
 ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
               "E4M3_F32": (1, 4)}
@@ -27,7 +27,7 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM",
 
 # C functions declared in include/distgemm.h (checked by the CPU tests)
 C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
-               "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
+               "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_plan_steps",
                "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                "dist_gemm_destroy", "dist_gemm_last_error", "dist_gemm_status_string")
 
@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_set_bias.argtypes = [vp, vp]
     lib.dist_gemm_set_option.argtypes = [vp, i32, i64]
     lib.dist_gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+    lib.dist_gemm_run_ag.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     lib.dist_gemm_plan_steps.argtypes = [vp, ctypes.POINTER(Step), ctypes.POINTER(i32)]
     lib.dist_gemm_step_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.dist_gemm_step_timeline.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
@@ -77,7 +78,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_status_string.argtypes = [i32]
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
     for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
-                 "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_plan_steps",
+                 "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_plan_steps",
                  "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                  "dist_gemm_destroy"):
         getattr(lib, name).restype = i32
@@ -146,6 +147,11 @@ def _stream(stream) -> Optional[int]:
 def dist_gemm_run(plan, A, B, C, D, alpha: float = 1.0, beta: float = 0.0, stream=None):
     _check(lib.dist_gemm_run(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), alpha, beta,
                              _stream(stream)), plan)
+
+
+def dist_gemm_run_ag(plan, A, B, C, D, ag_out, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    _check(lib.dist_gemm_run_ag(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(ag_out), alpha, beta,
+                                _stream(stream)), plan)
 
 
 def dist_gemm_plan_steps(plan) -> List[tuple]:
@@ -232,7 +238,7 @@ class Plan:
         if t.numel() * t.element_size() < nbytes:
             raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
 
-    def run(self, A, B, C, D, alpha=1.0, beta=0.0, stream=None):
+    def _check_operands(self, A, B, C, D):
         ei, eo = ELEM_BYTES[self.dtype]
         M, N, K, L = self.M, self.N, self.K, self.L
         self._need(A, (1 if self.shared_a else L) * M * K * ei, "A")
@@ -240,7 +246,21 @@ class Plan:
         self._need(D, L * M * N * eo, "D")
         if C is not None:
             self._need(C, L * M * N * eo, "C")
+
+    def run(self, A, B, C, D, alpha=1.0, beta=0.0, stream=None):
+        self._check_operands(A, B, C, D)
         dist_gemm_run(self.handle, A, B, C, D, alpha, beta, stream)
+
+    def run_ag(self, A, B, C, D, ag_out, alpha=1.0, beta=0.0, stream=None):
+        """run() that also writes the gathered rotating operand (A for AG_ROT_A,
+        B for AG_ROT_B) into ag_out."""
+        self._check_operands(A, B, C, D)
+        ei = ELEM_BYTES[self.dtype][0]
+        if _enum(SCHEDULES, self.schedule) == SCHEDULES["AG_ROT_A"]:
+            self._need(ag_out, (1 if self.shared_a else self.L) * self.M * self.K * ei, "ag_out")
+        else:
+            self._need(ag_out, self.L * self.N * self.K * ei, "ag_out")
+        dist_gemm_run_ag(self.handle, A, B, C, D, ag_out, alpha, beta, stream)
 
     def close(self):
         if self.handle is not None:

@@ -1,19 +1,22 @@
 // Host side of the TP-step GEMM library: validation, the step table, the
-// plan (staging slots, streams, events), the side-stream shard-copy engine
-// and the C ABI declared in include/distgemm.h.
+// plan (gathered staging image, streams, events, device tables), the
+// side-stream shard-copy engine, the single-launch tables and the C ABI
+// declared in include/distgemm.h.
 //
 // Mechanism (Distributed GEMM pull-request page, description): the operand
 // that arrives from a peer at every step is moved while the GEMM of the
 // current step runs, and each step's GEMM starts only after its operand is
 // in place.  On one GPU the peer's shard is a region of the caller's
-// operand, moved by a device-to-device hipMemcpyAsync into a staging slot on
-// a side stream, one copy per staged step, each followed by an event that
-// the launch computing the step waits on.  Copies go round-robin to up to
-// eight side streams, one per peer link that the transfer stands in for.
-// The copy is the library's streaming copy kernel by default (it runs
-// between GEMM workgroups); the runtime's device copy and the SDMA engine
-// (NoCU) are options -- measured, SDMA slows several-fold while the GEMMs
-// load memory.
+// operand, copied device to device into the same region of a gathered image
+// G of that operand (plan-owned, or the caller's gathered output).  By
+// default one persistent launch per run does everything (fused_run.h).  The
+// alternative execution launches the step GEMMs separately, with one copy
+// per staged step on side streams, each followed by an event that the launch
+// computing the step waits on.  Copies go round-robin to up to eight side
+// streams, one per peer link that the transfer stands in for; the copy is
+// the library's streaming copy kernel by default (it runs between GEMM
+// workgroups); the runtime's device copy and the SDMA engine (NoCU) are
+// options -- measured, SDMA slows several-fold while the GEMMs load memory.
 // Consecutive staged steps whose shards are adjacent may run as one GEMM
 // launch; launches alternate between the caller's stream and a second
 // compute stream (the stream alternation of the PyTorch symmetric-memory
@@ -117,7 +120,7 @@ std::vector<dist_gemm_step> build_steps(const Problem& p) {
     st.step = s;
     st.shard = j;
     st.staged = s > 0 ? 1 : 0;
-    st.slot = s > 0 ? s - 1 : -1;
+    st.slot = s > 0 ? j : -1;  // shard position in the gathered image
     if (rows) {
       st.m0 = j * w; st.m1 = (j + 1) * w; st.n0 = 0; st.n1 = p.N;
     } else {
@@ -128,46 +131,55 @@ std::vector<dist_gemm_step> build_steps(const Problem& p) {
   return v;
 }
 
-// Geometry of one staged shard: a 2-D region (height rows of width bytes,
-// src_pitch apart) of the source operand.  The staging buffer is height rows
-// of S-1 slots side by side: slot k occupies bytes [k*width, (k+1)*width) of
-// every staging row, and staging rows are (S-1)*width apart.  Consecutive
-// slots are therefore one contiguous region of every row, so the shards of
-// consecutive steps form one operand (or partial) matrix and their GEMMs can
-// run as one launch.
+// The gathered image G of the rotating operand has the operand's own layout:
+// shard j occupies, in G, the bytes it occupies in the operand -- `height`
+// rows of `width` bytes at offset j * width, rows `pitch` apart (one row per
+// batch for the row-contiguous shards; one row per row of C for the column
+// chunks of RS_TILE_B_ROT_C).  So a staged step reads G exactly where it
+// would read the operand, and the shards of consecutive steps are adjacent
+// in G as in the operand.
 struct CopyGeom {
-  size_t width = 0, height = 0, src_pitch = 0;
-  size_t staging_pitch(int slots) const { return width * static_cast<size_t>(slots); }
+  size_t width = 0, height = 0, pitch = 0;
+  size_t alloc = 0;  // bytes of the plan's G (sized for L batches also when A is shared)
 };
 
 CopyGeom copy_geom(const Problem& p) {
   CopyGeom g;
   const size_t S = static_cast<size_t>(p.S);
+  const size_t L = static_cast<size_t>(p.L);
   switch (p.schedule) {
     case DIST_GEMM_AG_ROT_A:  // A row shard, per batch contiguous (one batch if A is shared)
       g.width = static_cast<size_t>(p.M / S) * p.K * p.es_in;
-      g.height = p.shared_a ? 1 : p.L;
-      g.src_pitch = static_cast<size_t>(p.M) * p.K * p.es_in;
+      g.height = p.shared_a ? 1 : L;
+      g.pitch = static_cast<size_t>(p.M) * p.K * p.es_in;
+      g.alloc = L * g.pitch;
       break;
     case DIST_GEMM_AG_ROT_B:  // B column shard = rows of the N x K storage
       g.width = static_cast<size_t>(p.N / S) * p.K * p.es_in;
-      g.height = p.L;
-      g.src_pitch = static_cast<size_t>(p.N) * p.K * p.es_in;
+      g.height = L;
+      g.pitch = static_cast<size_t>(p.N) * p.K * p.es_in;
+      g.alloc = L * g.pitch;
       break;
     case DIST_GEMM_RS_TILE_A_ROT_C:  // C row chunk
       g.width = static_cast<size_t>(p.M / S) * p.N * p.es_out;
-      g.height = p.L;
-      g.src_pitch = static_cast<size_t>(p.M) * p.N * p.es_out;
+      g.height = L;
+      g.pitch = static_cast<size_t>(p.M) * p.N * p.es_out;
+      g.alloc = L * g.pitch;
       break;
     case DIST_GEMM_RS_TILE_B_ROT_C:  // C column chunk: one strip per row
       g.width = static_cast<size_t>(p.N / S) * p.es_out;
-      g.height = static_cast<size_t>(p.L) * p.M;
-      g.src_pitch = static_cast<size_t>(p.N) * p.es_out;
+      g.height = L * static_cast<size_t>(p.M);
+      g.pitch = static_cast<size_t>(p.N) * p.es_out;
+      g.alloc = g.height * g.pitch;
       break;
     default:
       break;
   }
   return g;
+}
+
+bool reduce_scatter(int schedule) {
+  return schedule == DIST_GEMM_RS_TILE_A_ROT_C || schedule == DIST_GEMM_RS_TILE_B_ROT_C;
 }
 
 }  // namespace
@@ -177,8 +189,7 @@ struct dist_gemm_plan_s {
   std::vector<dist_gemm_step> steps;
   CopyGeom geom;
   int device = 0;
-  uint8_t* staging = nullptr;
-  size_t staging_pitch = 0;  // bytes between staging rows: (S-1) slots of geom.width
+  uint8_t* staging = nullptr;  // the plan's gathered image G (geom.alloc bytes)
   std::vector<hipStream_t> sides;     // copy engine streams (created on demand)
   std::vector<hipEvent_t> ev_side_done;  // one per side stream
   hipStream_t cs2 = nullptr;   // second compute stream
@@ -192,26 +203,35 @@ struct dist_gemm_plan_s {
   // [run % step_timing][step] = first step of the launch that computed it
   // (launch events are recorded at that step's index).
   std::vector<int> t_first;
-  // Single-launch execution: device tables and counters (rotating plans only).
+  // Single-launch execution: device tables and counters (rotating plans
+  // only), allocated once at their largest size and never freed before the
+  // plan, so a captured run's kernel arguments stay valid.
   int execution = 1;
   int queues = dg::kMaxQueues;
   int64_t copy_chunk = 2 << 20;
   int64_t wait_limit_us = 1000000;
+  int64_t copy_delay_us = 0;   // test hook: copies start this late
   int64_t clock_khz = 100000;  // device wall clock rate
   int n_cu = 256;
-  dg::FusedStep* d_steps = nullptr;
-  int32_t* d_seg = nullptr;   // [queues][S + 1] then [queues][S] copy counts
+  int n_strips = 0;            // strips per batch of the rotating operand
+  dg::FusedSeg* d_segs = nullptr;        // [S]
+  dg::FusedStepCopy* d_copies = nullptr; // [S]
+  int32_t* d_strips = nullptr;           // [2][n_strips]: strip list, step of each position
+  int32_t* d_seg = nullptr;              // [kMaxQueues][S + 1]
+  uint32_t* d_ctr = nullptr;             // [L][n_strips] strip counters, [L][S] step counters
   int32_t* d_sync = nullptr;
-  uint64_t fused_align = 0;   // OR of the chunk widths (copy unit choice)
-  int fused_groups = 0;       // launch groups in the device tables
-  int copy_ahead = 4;         // copy lookahead, launch groups
+  uint64_t* d_times = nullptr;           // [step_timing][timeline_words(S)]
+  uint64_t fused_align = 0;   // OR of the piece sizes (copy unit choice)
+  int n_segs = 0;             // segments in the device tables
+  int copy_ahead = 4;         // copy lookahead, segments
+  bool captured = false;      // a run was captured into a graph: tables are fixed
   std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
   const void* bias = nullptr;  // device, N values of the output type, or NULL
   int compute_streams = 2;
   int copy_engine = 2;  // library streaming copy kernel
   int copy_streams = 2;
-  int max_group = 2;  // consecutive staged steps per launch
+  int max_group = 2;  // consecutive staged steps per launch / queue segment
   int step_timing = 0;
   int64_t timed_runs = 0;  // runs recorded since timing was (re)enabled
   bool has_prev = false;
@@ -248,9 +268,11 @@ void release(dist_gemm_plan_s* p) {
   for (hipStream_t s : p->sides) if (s) (void)hipStreamDestroy(s);
   if (p->cs2) (void)hipStreamDestroy(p->cs2);
   if (p->staging) (void)hipFree(p->staging);
-  if (p->d_steps) (void)hipFree(p->d_steps);
-  if (p->d_seg) (void)hipFree(p->d_seg);
-  if (p->d_sync) (void)hipFree(p->d_sync);
+  for (void* d : {static_cast<void*>(p->d_segs), static_cast<void*>(p->d_copies),
+                  static_cast<void*>(p->d_strips), static_cast<void*>(p->d_seg),
+                  static_cast<void*>(p->d_ctr), static_cast<void*>(p->d_sync),
+                  static_cast<void*>(p->d_times)})
+    if (d) (void)hipFree(d);
   delete p;
 }
 
@@ -326,26 +348,16 @@ hipError_t launch_shard_copy(uint8_t* dst, size_t dpitch, const uint8_t* src, si
   return hipGetLastError();
 }
 
-int enqueue_copy(dist_gemm_plan_s* P, hipStream_t side, const void* src_base, int shard, int slot) {
+// Copy shard `shard` of the rotating operand into the same region of the
+// gathered image G on `side`.
+int enqueue_copy(dist_gemm_plan_s* P, hipStream_t side, const void* src_base, uint8_t* G, int shard) {
   const CopyGeom& g = P->geom;
-  const Problem& pr = P->pr;
-  const uint8_t* src = static_cast<const uint8_t*>(src_base);
-  switch (pr.schedule) {
-    case DIST_GEMM_AG_ROT_A:
-    case DIST_GEMM_AG_ROT_B:
-    case DIST_GEMM_RS_TILE_A_ROT_C:
-      src += static_cast<size_t>(shard) * g.width;
-      break;
-    case DIST_GEMM_RS_TILE_B_ROT_C:
-      src += static_cast<size_t>(shard) * g.width;  // column offset within each row
-      break;
-    default:
-      return DIST_GEMM_OK;
-  }
-  uint8_t* dst = P->staging + static_cast<size_t>(slot) * g.width;
+  const size_t off = static_cast<size_t>(shard) * g.width;
+  const uint8_t* src = static_cast<const uint8_t*>(src_base) + off;
+  uint8_t* dst = G + off;
   hipError_t e;
   if (P->copy_engine == 2) {
-    e = launch_shard_copy(dst, P->staging_pitch, src, g.src_pitch, g.width, g.height, side);
+    e = launch_shard_copy(dst, g.pitch, src, g.pitch, g.width, g.height, side);
     if (e != hipSuccess) return hip_fail(&P->err, e, "shard copy kernel");
     return DIST_GEMM_OK;
   }
@@ -354,14 +366,21 @@ int enqueue_copy(dist_gemm_plan_s* P, hipStream_t side, const void* src_base, in
   if (g.height == 1)
     e = hipMemcpyAsync(dst, src, g.width, kind, side);
   else
-    e = hipMemcpy2DAsync(dst, P->staging_pitch, src, g.src_pitch, g.width, g.height, kind, side);
+    e = hipMemcpy2DAsync(dst, g.pitch, src, g.pitch, g.width, g.height, kind, side);
   if (e != hipSuccess) return hip_fail(&P->err, e, "shard copy");
   return DIST_GEMM_OK;
 }
 
+// Test hook of the step-launch execution: holds a side stream for `ticks`
+// of the device wall clock before its copies (one thread, bounded).
+__global__ void copy_delay_kernel(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
 // Launches of one run: consecutive staged steps whose shards are adjacent
-// (shard index and staging slot both one higher) merge, up to max_group
-// steps per launch; the unstaged step launches alone.
+// (shard index one higher, so adjacent in G as in the operand) merge, up to
+// max_group steps per launch; the unstaged step launches alone.
 struct LaunchGroup {
   int first, count;
 };
@@ -373,8 +392,7 @@ std::vector<LaunchGroup> group_steps(const dist_gemm_plan_s* P) {
     if (!v.empty() && P->pr.schedule != DIST_GEMM_MONOLITHIC) {
       LaunchGroup& b = v.back();
       const dist_gemm_step& prev = P->steps[b.first + b.count - 1];
-      const bool adjacent = s.staged && prev.staged && s.slot == prev.slot + 1 &&
-                            s.shard == prev.shard + 1;
+      const bool adjacent = s.staged && prev.staged && s.shard == prev.shard + 1;
       if (adjacent && b.count < P->max_group) {
         ++b.count;
         continue;
@@ -385,9 +403,10 @@ std::vector<LaunchGroup> group_steps(const dist_gemm_plan_s* P) {
   return v;
 }
 
-// Where step st's operands live: byte offsets from the caller's operands,
-// or (staged*) from the staging buffer, with leading dimensions and batch
-// strides in elements.
+// Where step st's operands live: byte offsets from the caller's operands
+// (G has the rotating operand's layout, so a staged operand is read at the
+// same offsets from G), with leading dimensions and batch strides in
+// elements.
 struct StepLayout {
   int64_t offA, offB, offC, offD, offBias;
   int64_t lda, ldb, ldc, ldd, sA, sB, sC, sD;
@@ -398,14 +417,10 @@ struct StepLayout {
 StepLayout step_layout(const dist_gemm_plan_s* P, const dist_gemm_step& st) {
   const Problem& pr = P->pr;
   const int64_t M = pr.M, N = pr.N, K = pr.K;
-  const int64_t S = pr.S;
   const int ei = pr.es_in, eo = pr.es_out;
-  const int64_t slot = st.staged ? static_cast<int64_t>(st.slot) * P->geom.width : 0;
-  const int64_t slots = S - 1;
   StepLayout y{};
   y.M = static_cast<int32_t>(st.m1 - st.m0);
   y.N = static_cast<int32_t>(st.n1 - st.n0);
-  // defaults: operands in place
   y.offA = st.m0 * K * ei;  y.lda = K; y.sA = pr.shared_a ? 0 : M * K;
   y.offB = st.n0 * K * ei;  y.ldb = K; y.sB = N * K;
   y.offC = (st.m0 * N + st.n0) * eo; y.ldc = N; y.sC = M * N;
@@ -413,13 +428,10 @@ StepLayout step_layout(const dist_gemm_plan_s* P, const dist_gemm_step& st) {
   y.offBias = st.n0 * eo;
   if (st.staged) {
     switch (pr.schedule) {
-      case DIST_GEMM_AG_ROT_A:
-        y.stagedA = true; y.offA = slot; y.sA = pr.shared_a ? 0 : slots * (M / S) * K; break;
-      case DIST_GEMM_AG_ROT_B: y.stagedB = true; y.offB = slot; y.sB = slots * (N / S) * K; break;
+      case DIST_GEMM_AG_ROT_A: y.stagedA = true; break;
+      case DIST_GEMM_AG_ROT_B: y.stagedB = true; break;
       case DIST_GEMM_RS_TILE_A_ROT_C:
-        y.stagedC = true; y.offC = slot; y.ldc = N; y.sC = slots * (M / S) * N; break;
-      case DIST_GEMM_RS_TILE_B_ROT_C:
-        y.stagedC = true; y.offC = slot; y.ldc = slots * (N / S); y.sC = M * slots * (N / S); break;
+      case DIST_GEMM_RS_TILE_B_ROT_C: y.stagedC = true; break;
       default: break;
     }
   }
@@ -428,9 +440,10 @@ StepLayout step_layout(const dist_gemm_plan_s* P, const dist_gemm_step& st) {
 
 // GEMM parameters of one step.
 dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, const void* A,
-                           const void* B, const void* C, void* D, float alpha, float beta) {
+                           const void* B, const void* C, void* D, const uint8_t* G, float alpha,
+                           float beta) {
   const StepLayout y = step_layout(P, st);
-  const uint8_t* stg = P->staging;
+  const uint8_t* stg = G;
   dg::GemmParams g{};
   g.K = static_cast<int32_t>(P->pr.K);
   g.L = static_cast<int32_t>(P->pr.L);
@@ -451,13 +464,14 @@ dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, 
 
 // GEMM parameters of a launch group: the first step's operands, extended
 // over the group's rows (row schedules) or columns.  The group's shards are
-// adjacent in the source operand, in the staging buffer and in D, so the
+// adjacent in the source operand, in G and in D, so the
 // extended views address exactly the member steps' data.
 dg::GemmParams group_params(const dist_gemm_plan_s* P, const LaunchGroup& grp, const void* A,
-                            const void* B, const void* C, void* D, float alpha, float beta) {
+                            const void* B, const void* C, void* D, const uint8_t* G, float alpha,
+                            float beta) {
   const dist_gemm_step& f = P->steps[grp.first];
   const dist_gemm_step& l = P->steps[grp.first + grp.count - 1];
-  dg::GemmParams g = step_params(P, f, A, B, C, D, alpha, beta);
+  dg::GemmParams g = step_params(P, f, A, B, C, D, G, alpha, beta);
   g.M = static_cast<int32_t>(std::max(f.m1, l.m1) - f.m0);
   g.N = static_cast<int32_t>(std::max(f.n1, l.n1) - f.n0);
   return g;
@@ -465,96 +479,220 @@ dg::GemmParams group_params(const dist_gemm_plan_s* P, const LaunchGroup& grp, c
 
 // ---- Single-launch execution ----------------------------------------------
 
-// Build the device tables of the single-launch run: the pointer-free table of
-// launch groups with their copy chunking, each queue's tile segments, and
-// zeroed counters.  Synchronous (plan creation and option changes only).
+// The rotating operand seen as strips of the monolithic tile grid.
+struct StripGeom {
+  int rot = 0, cols = 0, strided = 0;
+  int64_t ext = 0;        // rows (row strips) or columns (column strips)
+  int64_t row_bytes = 0;  // row strips: bytes per row; column strips: element bytes
+  int64_t gbatch = 0;     // bytes between batches
+  int64_t pitch = 0, height = 0;  // column strips: bytes between rows, rows per batch
+  int LG = 1;             // batches of G
+  int64_t strip_bytes = 0;  // bytes of one full strip of one batch
+};
+
+StripGeom strip_geom(const Problem& pr) {
+  StripGeom g;
+  const int64_t ei = pr.es_in, eo = pr.es_out;
+  switch (pr.schedule) {
+    case DIST_GEMM_AG_ROT_A:
+      g.rot = 0; g.ext = pr.M; g.row_bytes = pr.K * ei;
+      g.LG = pr.shared_a ? 1 : static_cast<int>(pr.L);
+      g.gbatch = pr.shared_a ? 0 : pr.M * pr.K * ei;
+      break;
+    case DIST_GEMM_AG_ROT_B:
+      g.rot = 1; g.cols = 1; g.ext = pr.N; g.row_bytes = pr.K * ei;
+      g.LG = static_cast<int>(pr.L); g.gbatch = pr.N * pr.K * ei;
+      break;
+    case DIST_GEMM_RS_TILE_A_ROT_C:
+      g.rot = 2; g.ext = pr.M; g.row_bytes = pr.N * eo;
+      g.LG = static_cast<int>(pr.L); g.gbatch = pr.M * pr.N * eo;
+      break;
+    case DIST_GEMM_RS_TILE_B_ROT_C:
+      g.rot = 2; g.cols = 1; g.ext = pr.N; g.row_bytes = eo;
+      g.LG = static_cast<int>(pr.L); g.gbatch = pr.M * pr.N * eo;
+      g.pitch = pr.N * eo; g.height = pr.M;
+      break;
+    default:
+      break;
+  }
+  // AG_ROT_B's strips are tile columns but 256 rows of the N x K storage:
+  // contiguous like A's; only RS_TILE_B_ROT_C's strips are strided
+  g.strided = pr.schedule == DIST_GEMM_RS_TILE_B_ROT_C ? 1 : 0;
+  g.strip_bytes = g.strided ? g.height * dg::kBN * g.row_bytes
+                                                           : static_cast<int64_t>(dg::kBM) * g.row_bytes;
+  return g;
+}
+
+// Allocate the single-launch tables at their largest size (once per plan).
+int alloc_fused(dist_gemm_plan_s* P, std::string* err) {
+  const Problem& pr = P->pr;
+  const int S = pr.S;
+  const StripGeom sg = strip_geom(pr);
+  P->n_strips = static_cast<int>((sg.ext + dg::kBM - 1) / dg::kBM);
+  const size_t n_ctr = static_cast<size_t>(pr.L) * (P->n_strips + S);
+  const size_t n_sync = static_cast<size_t>(dg::sync_words(S));
+  DG_HIP(err, hipMalloc(&P->d_segs, sizeof(dg::FusedSeg) * S));
+  DG_HIP(err, hipMalloc(&P->d_copies, sizeof(dg::FusedStepCopy) * S));
+  DG_HIP(err, hipMalloc(&P->d_strips, sizeof(int32_t) * 2 * P->n_strips));
+  DG_HIP(err, hipMalloc(&P->d_seg, sizeof(int32_t) * dg::kMaxQueues * (S + 1)));
+  DG_HIP(err, hipMalloc(&P->d_ctr, sizeof(uint32_t) * n_ctr));
+  DG_HIP(err, hipMalloc(&P->d_sync, sizeof(int32_t) * n_sync));
+  DG_HIP(err, hipMemset(P->d_ctr, 0, sizeof(uint32_t) * n_ctr));
+  DG_HIP(err, hipMemset(P->d_sync, 0, sizeof(int32_t) * n_sync));
+  return DIST_GEMM_OK;
+}
+
+// Build the single-launch tables: each strip's step (the latest step of the
+// shards it overlaps), the strip list by step, the queue segments (step 0,
+// then groups of max_group consecutive steps), which segment carries (or
+// claims) each step's copy, the piece size of each step, and each queue's
+// item ranges.  Synchronous (plan creation and option changes only).
 int build_fused(dist_gemm_plan_s* P, std::string* err) {
   const Problem& pr = P->pr;
   const int S = pr.S;
   const int nq = P->queues;
-  const CopyGeom& cg = P->geom;
-  const int64_t width = static_cast<int64_t>(cg.width), height = static_cast<int64_t>(cg.height);
+  const StripGeom sg = strip_geom(pr);
+  const int ns = P->n_strips;
+  const int64_t w = sg.ext / S;  // shard width along the strip dimension
+  const int64_t L = pr.L;
+  const int64_t other = sg.cols ? (pr.M + dg::kBM - 1) / dg::kBM : (pr.N + dg::kBN - 1) / dg::kBN;
 
-  // one table entry per launch group (the step-launch execution's grouping)
-  const std::vector<LaunchGroup> groups = group_steps(P);
-  const int G = static_cast<int>(groups.size());
-  std::vector<dg::FusedStep> fs(G);
-  for (int gi = 0; gi < G; ++gi) {
-    const LaunchGroup& grp = groups[gi];
-    const dist_gemm_step& st = P->steps[grp.first];
-    const dist_gemm_step& last = P->steps[grp.first + grp.count - 1];
-    const StepLayout y = step_layout(P, st);
-    dg::FusedStep& f = fs[gi];
-    f.offA = y.offA; f.offB = y.offB; f.offC = y.offC; f.offD = y.offD; f.offBias = y.offBias;
-    f.lda = y.lda; f.ldb = y.ldb; f.ldc = y.ldc; f.ldd = y.ldd;
-    f.sA = y.sA; f.sB = y.sB; f.sC = y.sC; f.sD = y.sD;
-    f.M = static_cast<int32_t>(std::max(st.m1, last.m1) - st.m0);
-    f.N = static_cast<int32_t>(std::max(st.n1, last.n1) - st.n0);
-    f.tiles_m = (f.M + dg::kBM - 1) / dg::kBM;
-    f.tiles_n = (f.N + dg::kBN - 1) / dg::kBN;
-    f.stagedA = y.stagedA; f.stagedB = y.stagedB; f.stagedC = y.stagedC;
-    f.copy_src_off = st.staged ? static_cast<int64_t>(st.shard) * width : 0;
-    f.copy_dst_off = st.staged ? static_cast<int64_t>(st.slot) * width : 0;
+  std::vector<int> step_of_shard(S, 0);
+  for (const dist_gemm_step& st : P->steps) step_of_shard[st.shard] = st.step;
+  std::vector<int> sstep(ns, 0);
+  for (int k = 0; k < ns; ++k) {
+    const int64_t r0 = static_cast<int64_t>(k) * dg::kBM;
+    const int64_t r1 = std::min<int64_t>(r0 + dg::kBM, sg.ext);
+    for (int64_t j = r0 / w; j <= (r1 - 1) / w; ++j) sstep[k] = std::max(sstep[k], step_of_shard[j]);
   }
-  // Copy chunking of group h: its bytes spread over the tiles of its carrier
-  // group max(0, h - D), about one chunk per tile (at most COPY_CHUNK bytes,
-  // at least 4 KiB, a multiple of 16), so that every carrier does about the
-  // same copy work.
-  for (int h = 0; h < G; ++h) {
-    dg::FusedStep& f = fs[h];
-    f.chunk_cols = width; f.chunk_rows = 1; f.chunks_per_row = 1; f.chunks_per_step = 0;
-    f.n_chunks = 0;
-    if (!P->steps[groups[h].first].staged) continue;
-    const dg::FusedStep& carrier = fs[std::max(0, h - P->copy_ahead)];
-    const int64_t ctiles = static_cast<int64_t>(carrier.tiles_m) * carrier.tiles_n * pr.L;
-    const int64_t bytes = width * height * groups[h].count;
-    int64_t chunk = (bytes + ctiles - 1) / ctiles;
-    chunk = std::min<int64_t>(P->copy_chunk, std::max<int64_t>(4096, (chunk + 15) / 16 * 16));
-    if (width >= chunk) {
-      f.chunk_cols = chunk;
-      f.chunks_per_row = static_cast<int32_t>((width + chunk - 1) / chunk);
-      f.chunk_rows = 1;
+  std::vector<int32_t> list, lstep;
+  std::vector<int> sfirst(S + 1, 0);
+  for (int h = 0; h < S; ++h) {
+    sfirst[h] = static_cast<int>(list.size());
+    for (int k = 0; k < ns; ++k)
+      if (sstep[k] == h) {
+        list.push_back(k);
+        lstep.push_back(h);
+      }
+  }
+  sfirst[S] = ns;
+
+  // segments
+  std::vector<std::pair<int, int>> segr;  // first and last step
+  segr.push_back({0, 0});
+  for (int h = 1; h < S; h += P->max_group) segr.push_back({h, std::min(S - 1, h + P->max_group - 1)});
+  const int G = static_cast<int>(segr.size());
+  std::vector<int> seg_of(S, 0);
+  std::vector<dg::FusedSeg> segs(G);
+  for (int g = 0; g < G; ++g) {
+    dg::FusedSeg& f = segs[g];
+    f.strip0 = sfirst[segr[g].first];
+    f.nst = sfirst[segr[g].second + 1] - f.strip0;
+    f.tiles = static_cast<int32_t>(f.nst * other);
+    f.carry_first = f.claim_first = S;
+    f.carry_last = f.claim_last = -1;
+    for (int h = segr[g].first; h <= segr[g].second; ++h) seg_of[h] = g;
+    if (static_cast<int64_t>(f.nst) * other * L >= INT32_MAX)
+      return fail(err, DIST_GEMM_ERR_SHAPE, "too many tiles for one launch");
+  }
+  // carriers: the latest segment with tiles at least D before the step's,
+  // else the first one before it, else the step's own tiles claim its copy
+  std::vector<dg::FusedStepCopy> cps(S);
+  for (int h = 0; h < S; ++h) {
+    dg::FusedStepCopy& c = cps[h];
+    c.strip0 = sfirst[h];
+    c.nst = sfirst[h + 1] - sfirst[h];
+    c.wait = h >= 1 ? 1 : 0;
+    c.P = 1;
+    c.piece = sg.strip_bytes;
+    c.n_chunks = 0;
+    if (c.nst == 0) continue;
+    int carrier = -1;
+    bool claim = false;
+    if (h == 0) {
+      carrier = 0;  // step 0's tiles never wait: they may carry their own strips
     } else {
-      f.chunk_cols = width;
-      f.chunks_per_row = 1;
-      f.chunk_rows = std::max<int64_t>(1, chunk / width);
+      const int sh = seg_of[h];
+      for (int g = sh - P->copy_ahead; g >= 0 && carrier < 0; --g)
+        if (segs[g].tiles > 0) carrier = g;
+      for (int g = 0; g < sh && carrier < 0; ++g)
+        if (segs[g].tiles > 0) carrier = g;
+      if (carrier < 0) {
+        carrier = sh;
+        claim = true;
+      }
     }
-    const int64_t per_step = (height + f.chunk_rows - 1) / f.chunk_rows * f.chunks_per_row;
-    if (per_step * groups[h].count > (int64_t{1} << 30))
-      return fail(err, DIST_GEMM_ERR_UNSUPPORTED, "too many copy chunks; raise DIST_GEMM_OPT_COPY_CHUNK");
-    f.chunks_per_step = static_cast<int32_t>(per_step);
-    f.n_chunks = static_cast<int32_t>(per_step * groups[h].count);
+    dg::FusedSeg& cs = segs[carrier];
+    if (claim) {
+      cs.claim_first = std::min(cs.claim_first, h);
+      cs.claim_last = std::max(cs.claim_last, h);
+    } else {
+      cs.carry_first = std::min(cs.carry_first, h);
+      cs.carry_last = std::max(cs.carry_last, h);
+    }
+    // pieces: about four per carrier tile over all the steps the carrier
+    // segment carries (so balanced contiguous ranges differ by a quarter at
+    // most), whole 32 KiB batches of the copy loop above that size, at
+    // least 4 KiB, at most COPY_CHUNK bytes
+    const int64_t ctiles = std::max<int64_t>(1, static_cast<int64_t>(cs.tiles) * L);
+    int64_t carried = 0;
+    for (int h2 = 0; h2 < S; ++h2) {
+      const int n2 = sfirst[h2 + 1] - sfirst[h2];
+      if (n2 == 0 || h2 == 0) continue;
+      int c2 = -1;
+      const int sh2 = seg_of[h2];
+      for (int g = sh2 - P->copy_ahead; g >= 0 && c2 < 0; --g)
+        if (segs[g].tiles > 0) c2 = g;
+      for (int g = 0; g < sh2 && c2 < 0; ++g)
+        if (segs[g].tiles > 0) c2 = g;
+      if (c2 < 0) c2 = sh2;
+      if (c2 == carrier) carried += n2;
+    }
+    if (h == 0) carried += c.nst;
+    const int64_t total = std::max<int64_t>(carried, c.nst) * sg.LG * sg.strip_bytes;
+    int64_t piece = (total + 4 * ctiles - 1) / (4 * ctiles);
+    piece = std::max<int64_t>(4096, (piece + 15) / 16 * 16);
+    if (piece > 32768) piece = (piece + 32767) / 32768 * 32768;
+    piece = std::min<int64_t>(P->copy_chunk, piece);
+    int64_t per;
+    if (!sg.strided) {
+      c.piece = piece;
+      per = (sg.strip_bytes + piece - 1) / piece;
+    } else {
+      c.piece = std::max<int64_t>(1, piece / (dg::kBN * sg.row_bytes));
+      per = (sg.height + c.piece - 1) / c.piece;
+    }
+    const int64_t n = per * c.nst * sg.LG;
+    if (n > (int64_t{1} << 30))
+      return fail(err, DIST_GEMM_ERR_UNSUPPORTED, "too many copy pieces; raise DIST_GEMM_OPT_COPY_CHUNK");
+    c.P = static_cast<int32_t>(per);
+    c.n_chunks = static_cast<int32_t>(n);
   }
-  P->fused_groups = G;
-  // queue q: its share of every group's tiles (a contiguous range of the
-  // group's tile order per batch), group after group
+  // (the carrier segment does not decrease with the step, so every segment
+  // carries a contiguous range of steps, and claims only steps of its own)
+  P->n_segs = G;
+  // queue q: its share of every segment's tiles (a contiguous range of the
+  // segment's tile order per batch), segment after segment
   std::vector<int32_t> seg(static_cast<size_t>(nq) * (G + 1), 0);
   for (int q = 0; q < nq; ++q) {
     int64_t at = 0;
-    for (int s = 0; s < G; ++s) {
-      seg[static_cast<size_t>(q) * (G + 1) + s] = static_cast<int32_t>(at);
-      const int64_t T2 = static_cast<int64_t>(fs[s].tiles_m) * fs[s].tiles_n;
-      at += (T2 / nq + (q < T2 % nq ? 1 : 0)) * pr.L;
-      if (at >= INT32_MAX || T2 * pr.L >= INT32_MAX)
-        return fail(err, DIST_GEMM_ERR_SHAPE, "too many tiles for one launch");
+    for (int g = 0; g < G; ++g) {
+      seg[static_cast<size_t>(q) * (G + 1) + g] = static_cast<int32_t>(at);
+      const int64_t T2 = segs[g].tiles;
+      at += (T2 / nq + (q < T2 % nq ? 1 : 0)) * L;
+      if (at >= INT32_MAX) return fail(err, DIST_GEMM_ERR_SHAPE, "too many tiles for one launch");
     }
     seg[static_cast<size_t>(q) * (G + 1) + G] = static_cast<int32_t>(at);
   }
-  const size_t sync_words = static_cast<size_t>(dg::kSyncDone + S) * dg::kSyncStride;
-  if (!P->d_steps) DG_HIP(err, hipMalloc(&P->d_steps, sizeof(dg::FusedStep) * S));
-  if (P->d_seg) {
-    DG_HIP(err, hipFree(P->d_seg));
-    P->d_seg = nullptr;
-  }
-  DG_HIP(err, hipMalloc(&P->d_seg, seg.size() * sizeof(int32_t)));
-  if (!P->d_sync) {
-    DG_HIP(err, hipMalloc(&P->d_sync, sync_words * sizeof(int32_t)));
-    DG_HIP(err, hipMemset(P->d_sync, 0, sync_words * sizeof(int32_t)));
-  }
-  DG_HIP(err, hipMemcpy(P->d_steps, fs.data(), sizeof(dg::FusedStep) * G, hipMemcpyHostToDevice));
+  std::vector<int32_t> strips(list);
+  strips.insert(strips.end(), lstep.begin(), lstep.end());
+  DG_HIP(err, hipMemcpy(P->d_segs, segs.data(), sizeof(dg::FusedSeg) * G, hipMemcpyHostToDevice));
+  DG_HIP(err, hipMemcpy(P->d_copies, cps.data(), sizeof(dg::FusedStepCopy) * S, hipMemcpyHostToDevice));
+  DG_HIP(err, hipMemcpy(P->d_strips, strips.data(), sizeof(int32_t) * strips.size(), hipMemcpyHostToDevice));
   DG_HIP(err, hipMemcpy(P->d_seg, seg.data(), seg.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   P->fused_align = 0;
-  for (const dg::FusedStep& f : fs) P->fused_align |= static_cast<uint64_t>(f.chunk_cols);
+  for (const dg::FusedStepCopy& c : cps)
+    if (!sg.strided) P->fused_align |= static_cast<uint64_t>(c.piece);
   return DIST_GEMM_OK;
 }
 
@@ -571,32 +709,53 @@ FusedOrder& fused_order() {
 }
 
 int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B, const void* C,
-              void* D, float alpha, float beta, const void* copy_src) {
+              void* D, uint8_t* G, float alpha, float beta, const void* copy_src, bool copy_on,
+              bool copy_local, uint64_t* times, uint64_t* times_next) {
   const Problem& pr = P->pr;
-  const CopyGeom& g = P->geom;
+  const StripGeom sg = strip_geom(pr);
   dg::FusedArgs a{};
-  a.A = A; a.B = B; a.C = beta != 0.0f ? C : nullptr; a.D = D;
-  a.bias = P->bias;
-  a.staging = P->staging;
-  a.copy_src = copy_src;
-  a.steps = P->d_steps;
+  dg::GemmParams& g = a.g;
+  g.A = A; g.B = B; g.C = beta != 0.0f ? C : nullptr; g.D = D;
+  g.bias = P->bias;
+  g.lda = pr.K; g.ldb = pr.K; g.ldc = pr.N; g.ldd = pr.N;
+  g.sA = pr.shared_a ? 0 : pr.M * pr.K; g.sB = pr.N * pr.K; g.sC = pr.M * pr.N; g.sD = pr.M * pr.N;
+  g.M = static_cast<int32_t>(pr.M); g.N = static_cast<int32_t>(pr.N);
+  g.K = static_cast<int32_t>(pr.K); g.L = static_cast<int32_t>(pr.L);
+  g.alpha = alpha; g.beta = beta;
+  a.gath = G;
+  a.src = static_cast<const uint8_t*>(copy_src);
+  a.segs = P->d_segs;
+  a.steps = P->d_copies;
+  a.strip_list = P->d_strips;
+  a.strip_step = P->d_strips + P->n_strips;
   a.seg = P->d_seg;
   a.sync = P->d_sync;
-  a.cp_width = static_cast<int64_t>(g.width);
-  a.cp_height = static_cast<int64_t>(g.height);
-  a.cp_src_pitch = static_cast<int64_t>(g.src_pitch);
-  a.cp_dst_pitch = static_cast<int64_t>(P->staging_pitch);
+  a.ctr = P->d_ctr;
+  a.times = times;
+  a.times_next = times_next;
+  a.row_bytes = sg.row_bytes;
+  a.ext = sg.ext;
+  a.gbatch = sg.gbatch;
+  a.pitch = sg.pitch;
+  a.height = sg.height;
   a.spin_limit = P->wait_limit_us * P->clock_khz / 1000;
-  const uint64_t align = reinterpret_cast<uint64_t>(copy_src) | reinterpret_cast<uint64_t>(P->staging) |
-                         g.src_pitch | P->staging_pitch | g.width | P->fused_align;
+  a.delay = P->copy_delay_us * P->clock_khz / 1000;
+  a.rot = sg.rot;
+  a.cols = sg.cols;
+  a.strided = sg.strided;
+  a.n_strips = P->n_strips;
+  a.LG = sg.LG;
+  uint64_t align = reinterpret_cast<uint64_t>(copy_src) | reinterpret_cast<uint64_t>(G) |
+                   static_cast<uint64_t>(sg.row_bytes) | static_cast<uint64_t>(sg.gbatch) | P->fused_align;
+  if (sg.strided)
+    align |= static_cast<uint64_t>(sg.pitch) | static_cast<uint64_t>(dg::kBN * sg.row_bytes) |
+             static_cast<uint64_t>(sg.ext * sg.row_bytes);
   a.unit = (align % 16 == 0) ? 16 : (align % 4 == 0) ? 4 : 1;
-  a.S = P->fused_groups;
-  a.K = static_cast<int32_t>(pr.K);
-  a.L = static_cast<int32_t>(pr.L);
+  a.n_seg = P->n_segs;
   a.nq = P->queues;
-  a.ahead = P->copy_ahead;
-  a.alpha = alpha;
-  a.beta = beta;
+  a.S = pr.S;
+  a.copy_on = copy_on ? 1 : 0;
+  a.copy_local = copy_local ? 1 : 0;
   const int grid = std::max(P->queues, P->n_cu / P->queues * P->queues);
 
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -618,6 +777,28 @@ int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B,
     o.live[P->device] = 1;
   }
   return DIST_GEMM_OK;
+}
+
+// Change a plan setting that the single-launch tables depend on: wait for
+// the plan's last run, apply, rebuild; on failure restore and rebuild.  A
+// plan whose run has been captured into a graph keeps its tables (the graph
+// holds their addresses and sizes in its kernel arguments).
+template <typename Apply, typename Undo>
+int change_tables(dist_gemm_plan_t plan, Apply apply, Undo undo) {
+  if (plan->captured)
+    return fail(&plan->err, DIST_GEMM_ERR_UNSUPPORTED,
+                "a run of this plan was captured into a graph: options that rebuild its device "
+                "tables (queues, copy chunk, copy lookahead, step group, shared A) are fixed");
+  DeviceGuard guard(plan->device);
+  if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
+  apply();
+  if (!plan->d_segs) return DIST_GEMM_OK;  // no staged steps: nothing to rebuild
+  const int rc = build_fused(plan, &plan->err);
+  if (rc != DIST_GEMM_OK) {
+    undo();
+    (void)build_fused(plan, nullptr);
+  }
+  return rc;
 }
 
 }  // namespace
@@ -678,15 +859,13 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
   P->steps = build_steps(pr);
   P->geom = copy_geom(pr);
   std::string* perr = nullptr;  // errors before the handle is returned go to the thread slot
-  const int n_slots = pr.S - 1;
-  if (pr.schedule != DIST_GEMM_MONOLITHIC && n_slots > 0) {
-    P->staging_pitch = P->geom.staging_pitch(n_slots);
-    e = hipMalloc(&P->staging, P->staging_pitch * P->geom.height);
+  const bool rotating = pr.schedule != DIST_GEMM_MONOLITHIC && pr.S > 1;
+  if (rotating) {
+    e = hipMalloc(&P->staging, P->geom.alloc);
     if (e != hipSuccess) {
       release(P);
       (void)hipGetLastError();
-      return fail(perr, DIST_GEMM_ERR_OOM, "staging allocation of " +
-                                               std::to_string(P->staging_pitch * P->geom.height) + " bytes");
+      return fail(perr, DIST_GEMM_ERR_OOM, "staging allocation of " + std::to_string(P->geom.alloc) + " bytes");
     }
   }
   auto mk = [&](hipEvent_t* ev, unsigned flags) { return hipEventCreateWithFlags(ev, flags); };
@@ -709,10 +888,12 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     P->clock_khz = khz;
-  if (pr.schedule != DIST_GEMM_MONOLITHIC && n_slots > 0) {
-    rc = build_fused(P, perr);
+  if (rotating) {
+    rc = alloc_fused(P, perr);
+    if (rc == DIST_GEMM_OK) rc = build_fused(P, perr);
     if (rc != DIST_GEMM_OK) {
       release(P);
+      (void)hipGetLastError();
       return rc;
     }
   }
@@ -762,87 +943,58 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       if (value < 1 || value > 1024)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "step group must be 1..1024");
       if (plan->max_group == value) return DIST_GEMM_OK;
-      const int old_g = plan->max_group;
-      plan->max_group = static_cast<int>(value);
-      if (!plan->d_steps) return DIST_GEMM_OK;
-      DeviceGuard guard(plan->device);
-      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
-      const int rc = build_fused(plan, &plan->err);
-      if (rc != DIST_GEMM_OK) {
-        plan->max_group = old_g;
-        (void)build_fused(plan, nullptr);
-      }
-      return rc;
+      const int old = plan->max_group;
+      return change_tables(plan, [&] { plan->max_group = static_cast<int>(value); },
+                           [&] { plan->max_group = old; });
     }
     case DIST_GEMM_OPT_EXECUTION:
       if (value != 0 && value != 1)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "execution must be 0 or 1");
       plan->execution = static_cast<int>(value);
       return DIST_GEMM_OK;
-    case DIST_GEMM_OPT_QUEUES:
-    case DIST_GEMM_OPT_COPY_CHUNK: {
-      const bool queues = option == DIST_GEMM_OPT_QUEUES;
-      if (queues && value != 1 && value != dg::kMaxQueues)
+    case DIST_GEMM_OPT_QUEUES: {
+      if (value != 1 && value != dg::kMaxQueues)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "queues must be 1 or 8");
-      if (!queues && (value < 4096 || value > (int64_t{1} << 28) || value % 16 != 0))
+      if (plan->queues == value) return DIST_GEMM_OK;
+      const int old = plan->queues;
+      return change_tables(plan, [&] { plan->queues = static_cast<int>(value); },
+                           [&] { plan->queues = old; });
+    }
+    case DIST_GEMM_OPT_COPY_CHUNK: {
+      if (value < 4096 || value > (int64_t{1} << 28) || value % 16 != 0)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG,
                     "copy chunk must be a multiple of 16 in [4096, 2^28]");
-      if ((queues ? plan->queues : plan->copy_chunk) == value) return DIST_GEMM_OK;
-      const int old_q = plan->queues;
-      const int64_t old_c = plan->copy_chunk;
-      if (queues)
-        plan->queues = static_cast<int>(value);
-      else
-        plan->copy_chunk = value;
-      if (!plan->d_steps) return DIST_GEMM_OK;  // no staged steps: nothing to rebuild
-      DeviceGuard guard(plan->device);
-      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
-      const int rc = build_fused(plan, &plan->err);
-      if (rc != DIST_GEMM_OK) {
-        plan->queues = old_q;
-        plan->copy_chunk = old_c;
-        (void)build_fused(plan, nullptr);
-      }
-      return rc;
+      if (plan->copy_chunk == value) return DIST_GEMM_OK;
+      const int64_t old = plan->copy_chunk;
+      return change_tables(plan, [&] { plan->copy_chunk = value; }, [&] { plan->copy_chunk = old; });
     }
     case DIST_GEMM_OPT_COPY_AHEAD: {
       if (value < 1 || value > 64)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy lookahead must be 1..64");
       if (plan->copy_ahead == value) return DIST_GEMM_OK;
-      const int old_a = plan->copy_ahead;
-      plan->copy_ahead = static_cast<int>(value);
-      if (!plan->d_steps) return DIST_GEMM_OK;
-      DeviceGuard guard(plan->device);
-      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
-      const int rc = build_fused(plan, &plan->err);
-      if (rc != DIST_GEMM_OK) {
-        plan->copy_ahead = old_a;
-        (void)build_fused(plan, nullptr);
-      }
-      return rc;
+      const int old = plan->copy_ahead;
+      return change_tables(plan, [&] { plan->copy_ahead = static_cast<int>(value); },
+                           [&] { plan->copy_ahead = old; });
     }
     case DIST_GEMM_OPT_SHARED_A: {
       if (value != 0 && value != 1)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "shared A must be 0 or 1");
       if (plan->pr.shared_a == (value != 0)) return DIST_GEMM_OK;
-      DeviceGuard guard(plan->device);
-      if (plan->has_prev) DG_HIP(&plan->err, hipEventSynchronize(plan->ev_done));
-      // the staging buffer was sized for L batches: a shared A needs one
-      plan->pr.shared_a = value != 0;
-      plan->geom = copy_geom(plan->pr);
-      if (!plan->d_steps) return DIST_GEMM_OK;
-      const int rc = build_fused(plan, &plan->err);
-      if (rc != DIST_GEMM_OK) {
+      auto flip = [&] {
         plan->pr.shared_a = !plan->pr.shared_a;
         plan->geom = copy_geom(plan->pr);
-        (void)build_fused(plan, nullptr);
-      }
-      return rc;
+      };
+      return change_tables(plan, flip, flip);
     }
     case DIST_GEMM_OPT_WAIT_LIMIT_US:
       if (value < 0 || value > 100000000)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "wait limit must be in [0, 1e8] us");
       plan->wait_limit_us = value;
+      return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_COPY_DELAY_US:
+      if (value < 0 || value > 1000000)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy delay must be in [0, 1e6] us");
+      plan->copy_delay_us = value;
       return DIST_GEMM_OK;
     case DIST_GEMM_OPT_STEP_TIMING: {
       if (value < 0 || value > 4096)
@@ -853,6 +1005,8 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       for (hipEvent_t ev : plan->t_end) if (ev) (void)hipEventDestroy(ev);
       for (hipEvent_t ev : plan->t_run0) if (ev) (void)hipEventDestroy(ev);
       for (hipEvent_t ev : plan->t_copy) if (ev) (void)hipEventDestroy(ev);
+      if (plan->d_times) (void)hipFree(plan->d_times);
+      plan->d_times = nullptr;
       plan->t_first.clear();
       plan->t_fused.clear();
       plan->t_begin.clear();
@@ -861,6 +1015,7 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       plan->t_copy.clear();
       plan->step_timing = 0;
       plan->timed_runs = 0;
+      if (value == 0) return DIST_GEMM_OK;
       const size_t n = static_cast<size_t>(value) * plan->steps.size();
       plan->t_begin.assign(n, nullptr);
       plan->t_end.assign(n, nullptr);
@@ -878,6 +1033,11 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
         const hipError_t e = hipEventCreate(&ev);
         if (e != hipSuccess) return hip_fail(&plan->err, e, "timing event creation");
       }
+      if (plan->d_segs) {
+        const size_t words = static_cast<size_t>(value) * dg::timeline_words(plan->pr.S);
+        DG_HIP(&plan->err, hipMalloc(&plan->d_times, words * sizeof(uint64_t)));
+        DG_HIP(&plan->err, hipMemset(plan->d_times, 0, words * sizeof(uint64_t)));
+      }
       plan->step_timing = static_cast<int>(value);
       return DIST_GEMM_OK;
     }
@@ -886,45 +1046,63 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
   }
 }
 
-int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
-                  float alpha, float beta, void* stream) {
+namespace {
+
+int run_impl(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D, void* ag_out,
+             float alpha, float beta, void* stream) {
   if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
   dist_gemm_plan_s* P = plan;
+  const Problem& pr = P->pr;
   if (!A || !B || !D) return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "A, B and D must be non-NULL");
   if (beta != 0.0f && !C) return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "C is NULL but beta != 0");
   if (!std::isfinite(alpha) || !std::isfinite(beta))
     return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "alpha and beta must be finite");
   if (D == A || D == B) return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "D must not alias A or B");
+  const bool ag = pr.schedule == DIST_GEMM_AG_ROT_A || pr.schedule == DIST_GEMM_AG_ROT_B;
+  if (ag_out) {
+    if (!ag)
+      return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG,
+                  "a gathered output exists only for the all-gather schedules");
+    if (ag_out == A || ag_out == B || ag_out == C || ag_out == D)
+      return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "ag_out must not alias A, B, C or D");
+  }
 
   DeviceGuard guard(P->device);
-  const Problem& pr = P->pr;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  DG_HIP(&P->err, hipStreamIsCapturing(st, &cap));
+  if (cap != hipStreamCaptureStatusNone) P->captured = true;
   const bool rotating = pr.schedule != DIST_GEMM_MONOLITHIC && pr.S > 1;
+  // a reduce-scatter with beta = 0 reads no partial: nothing rotates
+  const bool copy_on = rotating && !(reduce_scatter(pr.schedule) && beta == 0.0f);
   const bool two = P->compute_streams == 2 && pr.S > 1;
   const float alpha_eff =
       (pr.in_kind == dg::IN_E4M3) ? alpha * P->scale_a * P->scale_b : alpha;
-  const void* copy_src = nullptr;
-  switch (pr.schedule) {
-    case DIST_GEMM_AG_ROT_A: copy_src = A; break;
-    case DIST_GEMM_AG_ROT_B: copy_src = B; break;
-    default: copy_src = C; break;  // RS: the rotating partial
-  }
-  if (rotating && !copy_src) {
-    return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG,
-                "the reduce-scatter schedules rotate C: C must be non-NULL");
-  }
+  const void* copy_src = pr.schedule == DIST_GEMM_AG_ROT_A ? A : pr.schedule == DIST_GEMM_AG_ROT_B ? B : C;
+  uint8_t* G = ag_out ? static_cast<uint8_t*>(ag_out) : P->staging;
 
   if (rotating && P->execution == 1) {
     if (P->has_prev && P->prev_stream != st) DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_done, 0));
     const size_t trun = P->step_timing ? static_cast<size_t>(P->timed_runs % P->step_timing) : 0;
     const size_t tbase = trun * P->steps.size();
+    uint64_t* times = nullptr;
+    uint64_t* times_next = nullptr;
     if (P->step_timing) {
+      // every slot starts zeroed (at allocation); a launch zeroes the next
+      // slot of the ring at its end (one slot: zeroed before the launch)
+      const size_t words = dg::timeline_words(pr.S);
+      times = P->d_times + trun * words;
       DG_HIP(&P->err, hipEventRecord(P->t_run0[trun], st));
+      if (P->step_timing > 1)
+        times_next = P->d_times + ((trun + 1) % P->step_timing) * words;
+      else
+        DG_HIP(&P->err, hipMemsetAsync(times, 0, words * sizeof(uint64_t), st));
       for (size_t k = 0; k < P->steps.size(); ++k) P->t_first[tbase + k] = 0;
       P->t_fused[trun] = 1;
       DG_HIP(&P->err, hipEventRecord(P->t_begin[tbase], st));
     }
-    const int rc = run_fused(P, st, A, B, C, D, alpha_eff, beta, copy_src);
+    const int rc = run_fused(P, st, A, B, C, D, G, alpha_eff, beta, copy_src, copy_on, ag_out != nullptr, times,
+                             times_next);
     if (rc != DIST_GEMM_OK) return rc;
     if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[tbase], st));
     DG_HIP(&P->err, hipEventRecord(P->ev_done, st));
@@ -935,9 +1113,12 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
   }
 
   // side streams in use: the first n, n = min(copy streams, staged copies)
-  const int n_side = rotating ? std::min(P->copy_streams, pr.S - 1) : 0;
-  if (n_side > static_cast<int>(P->sides.size()))
-    return fail(&P->err, DIST_GEMM_ERR_INVALID_ARG, "copy streams not created");
+  const int n_copies = (copy_on ? pr.S - 1 : 0) + (ag_out ? 1 : 0);
+  const int n_side = n_copies > 0 ? std::max(1, std::min(P->copy_streams, std::max(pr.S - 1, 1))) : 0;
+  if (n_side > 0) {
+    const int rc = ensure_sides(P, n_side, &P->err);
+    if (rc != DIST_GEMM_OK) return rc;
+  }
 
   if (P->has_prev && P->prev_stream != st) DG_HIP(&P->err, hipStreamWaitEvent(st, P->ev_done, 0));
   DG_HIP(&P->err, hipEventRecord(P->ev_start, st));
@@ -945,22 +1126,33 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
   const size_t tbase = trun * P->steps.size();
   if (P->step_timing) {
     DG_HIP(&P->err, hipEventRecord(P->t_run0[trun], st));
-    P->t_fused[trun] = 0;
+    P->t_fused[trun] = copy_on ? 0 : 2;  // 2: step launches, nothing copied
   }
   for (int k = 0; k < n_side; ++k) DG_HIP(&P->err, hipStreamWaitEvent(P->sides[k], P->ev_start, 0));
   if (two) DG_HIP(&P->err, hipStreamWaitEvent(P->cs2, P->ev_start, 0));
+  if (P->copy_delay_us > 0)
+    for (int k = 0; k < n_side; ++k) {
+      hipLaunchKernelGGL(copy_delay_kernel, dim3(1), dim3(1), 0, P->sides[k],
+                         static_cast<uint64_t>(P->copy_delay_us * P->clock_khz / 1000));
+      DG_HIP(&P->err, hipGetLastError());
+    }
 
   // Copy engine: every staged operand, in step order, round-robin over the
-  // side streams, one event per copy.
-  if (rotating) {
+  // side streams, one event per copy; with a gathered output, the local
+  // shard last.
+  if (copy_on) {
     for (const dist_gemm_step& s : P->steps) {
       if (!s.staged) continue;
-      hipStream_t side = P->sides[s.slot % n_side];
-      int rc = enqueue_copy(P, side, copy_src, s.shard, s.slot);
+      hipStream_t side = P->sides[(s.step - 1) % n_side];
+      int rc = enqueue_copy(P, side, copy_src, G, s.shard);
       if (rc != DIST_GEMM_OK) return rc;
       DG_HIP(&P->err, hipEventRecord(P->ev_copy[s.step], side));
       if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_copy[tbase + s.step], side));
     }
+  }
+  if (ag_out) {
+    const int rc = enqueue_copy(P, P->sides[0], copy_src, G, P->steps[0].shard);
+    if (rc != DIST_GEMM_OK) return rc;
   }
   // Step GEMMs: one launch per group, alternating compute streams by launch.
   const std::vector<LaunchGroup> groups = group_steps(P);
@@ -968,11 +1160,11 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
     const LaunchGroup& grp = groups[gi];
     hipStream_t cs = (two && (gi & 1)) ? P->cs2 : st;
     for (int k = grp.first; k < grp.first + grp.count; ++k) {
-      if (P->steps[k].staged) DG_HIP(&P->err, hipStreamWaitEvent(cs, P->ev_copy[k], 0));
+      if (copy_on && P->steps[k].staged) DG_HIP(&P->err, hipStreamWaitEvent(cs, P->ev_copy[k], 0));
       if (P->step_timing) P->t_first[tbase + k] = grp.first;
     }
     if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_begin[tbase + grp.first], cs));
-    const dg::GemmParams g = group_params(P, grp, A, B, C, D, alpha_eff, beta);
+    const dg::GemmParams g = group_params(P, grp, A, B, C, D, copy_on ? G : nullptr, alpha_eff, beta);
     DG_HIP(&P->err, dg::launch_gemm(pr.in_kind, pr.out_kind, g, cs));
     if (P->step_timing) DG_HIP(&P->err, hipEventRecord(P->t_end[tbase + grp.first], cs));
   }
@@ -990,6 +1182,19 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
   P->prev_stream = st;
   if (P->step_timing) ++P->timed_runs;
   return DIST_GEMM_OK;
+}
+
+}  // namespace
+
+int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
+                  float alpha, float beta, void* stream) {
+  return run_impl(plan, A, B, C, D, nullptr, alpha, beta, stream);
+}
+
+int dist_gemm_run_ag(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
+                     void* ag_out, float alpha, float beta, void* stream) {
+  if (!ag_out) return fail(plan ? &plan->err : nullptr, DIST_GEMM_ERR_INVALID_ARG, "ag_out is NULL");
+  return run_impl(plan, A, B, C, D, ag_out, alpha, beta, stream);
 }
 
 int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_steps) {
@@ -1040,17 +1245,37 @@ int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n) {
   const size_t run = static_cast<size_t>((plan->timed_runs - 1) % plan->step_timing);
   const size_t base = run * static_cast<size_t>(S);
   hipEvent_t t0 = plan->t_run0[run];
-  for (int64_t s = 0; s < S; ++s) {
-    float v[3] = {-1.0f, 0.0f, 0.0f};
-    const bool staged = plan->steps[s].staged && plan->pr.schedule != DIST_GEMM_MONOLITHIC &&
-                        !plan->t_fused[run];
-    if (staged) DG_HIP(&plan->err, hipEventElapsedTime(&v[0], t0, plan->t_copy[base + s]));
-    const int f = plan->t_first[base + s];
-    DG_HIP(&plan->err, hipEventElapsedTime(&v[1], t0, plan->t_begin[base + f]));
-    DG_HIP(&plan->err, hipEventElapsedTime(&v[2], t0, plan->t_end[base + f]));
-    for (int k = 0; k < 3; ++k)
-      if (3 * s + k < cap) ms[3 * s + k] = v[k];
+  std::vector<float> v(3 * S, -1.0f);
+  if (plan->t_fused[run] == 1 && plan->d_times) {
+    // one launch: the device's own stamps (wall-clock ticks), placed on the
+    // run's time line by the launch's start event
+    const size_t words = dg::timeline_words(plan->pr.S);
+    std::vector<uint64_t> t(words);
+    DG_HIP(&plan->err, hipMemcpy(t.data(), plan->d_times + run * words, words * sizeof(uint64_t),
+                                 hipMemcpyDeviceToHost));
+    float launch0 = 0.0f;
+    DG_HIP(&plan->err, hipEventElapsedTime(&launch0, t0, plan->t_begin[base]));
+    const uint64_t start = ~t[0];
+    const double per_ms = static_cast<double>(plan->clock_khz);
+    auto at = [&](uint64_t tick) {
+      return static_cast<float>(launch0 + static_cast<double>(static_cast<int64_t>(tick - start)) / per_ms);
+    };
+    for (int64_t s = 0; s < S; ++s) {
+      if (t[1 + 3 * s]) v[3 * s] = at(t[1 + 3 * s]);
+      if (t[2 + 3 * s]) v[3 * s + 1] = at(~t[2 + 3 * s]);
+      if (t[3 + 3 * s]) v[3 * s + 2] = at(t[3 + 3 * s]);
+    }
+  } else {
+    for (int64_t s = 0; s < S; ++s) {
+      const bool staged = plan->steps[s].staged && plan->pr.schedule != DIST_GEMM_MONOLITHIC &&
+                          plan->t_fused[run] == 0;
+      if (staged) DG_HIP(&plan->err, hipEventElapsedTime(&v[3 * s], t0, plan->t_copy[base + s]));
+      const int f = plan->t_first[base + s];
+      DG_HIP(&plan->err, hipEventElapsedTime(&v[3 * s + 1], t0, plan->t_begin[base + f]));
+      DG_HIP(&plan->err, hipEventElapsedTime(&v[3 * s + 2], t0, plan->t_end[base + f]));
+    }
   }
+  for (int64_t k = 0; k < 3 * S && k < cap; ++k) ms[k] = v[k];
   *n = static_cast<int>(3 * S);
   return DIST_GEMM_OK;
 }

@@ -1,56 +1,72 @@
 // fused_run.h -- the whole TP-step schedule of one run as a single persistent
 // launch on gfx950: the workgroups perform the shard rotation (copy chunks)
-// and the step GEMMs (256 x 256 tiles), and a tile of a staged step starts
-// only once its step's shard is complete.
+// and every tile of the problem's monolithic 256 x 256 tile grid, and a tile
+// that reads a staged shard starts only once the part of the gathered
+// operand it reads is complete.
 //
 // This is the per-step readiness of the Distributed GEMM pull-request page
 // (each step's GEMM waits, at its start, for the operand its peer sent;
 // described there as a few barriers at the beginning of every GEMM kernel),
-// kept on the device: one counter per step, raised once per finished chunk,
-// so the steps run back to back inside one launch with no partly filled wave
-// between them.  The copy is done by the CUs because the SDMA engines slow
+// made tile-granular as in the TransformerEngine issue on overlapping
+// tensor-parallel collectives with matmuls (a GEMM that reports finished
+// tiles through atomic switches): one counter per strip -- the 256 rows (or
+// columns) of the rotating operand that one tile row (or column) reads --
+// raised once per finished copy piece, so a tile waits only for the rows it
+// reads.  The copy is done by the CUs because the SDMA engines slow
 // several-fold under the GEMM's memory traffic on this part.
 //
-// Steps.  The unit of the launch is a launch group: consecutive steps on
-// adjacent shards, computed as one GEMM over their union (as the step-launch
-// execution merges them), which keeps steps narrower than a tile from
-// leaving partly empty tiles; "group" below means such a group.
+// Tiles.  The launch computes the monolithic tile grid.  The rotating
+// operand (A, B, or the partial C) is gathered into an image G with the
+// operand's own layout; a strip's step is the latest step, in rotation
+// order, of the shards it overlaps.  Strips of step 0 lie inside the local
+// shard and are read in place; every other strip is copied whole into G
+// (the local-shard rows of a strip that straddles a shard boundary too) and
+// read from there.  Every output element is computed by the same tile code
+// with the same K order as the monolithic GEMM, so the result is bitwise the
+// monolithic one.
 //
-// Work distribution.  The work items are the tiles.  Workgroup b takes them
-// from queue b mod nq (nq = 8: MI355X places workgroup b on XCD b mod 8, so
-// every XCD has its own queue and runs one contiguous range of each group's
-// tile order, as the per-launch kernel does; nq = 1: one queue for the
-// chip), in queue order, by an atomic counter: queue q lists its tiles of
-// group 0, then of group 1, and so on.  The shard copies ride on the tiles:
-// the copy of group h is cut into chunks of about equal size, one or a few
-// per tile of group max(0, h - D) (D = a.ahead >= 1, the copy lookahead),
-// and a tile performs the chunks it carries before it waits for anything
-// and before its own GEMM.  Separate copy items would make the workgroups
-// of an XCD start their tiles out of phase, and tiles that run in phase
-// share each K slab of A and B in the XCD's L2: measured, copy items nearly
-// doubled the launch's HBM reads, while equal chunks on every tile keep the
-// tiles in phase.
+// Work distribution.  Workgroup b takes tiles from queue b mod nq (nq = 8:
+// MI355X places workgroup b on XCD b mod 8, so every XCD runs one
+// contiguous range of each segment's tile order, walked in groups of four
+// strips; nq = 1: one queue for the chip), in queue order, by an atomic
+// counter: queue q lists its tiles of segment 0 (step 0), then of segment
+// 1 (the next steps), and so on.  The shard copies ride on the tiles: the
+// copy of step h is cut into pieces of its strips, carried by the tiles of
+// an earlier segment (about D segments before h's, D = the copy lookahead),
+// and a tile performs the pieces it carries before it waits for anything
+// and before its own GEMM.  Equal pieces on every carrier keep the tiles of
+// an XCD in phase, so they share each K slab of A and B in the XCD's L2.
+// A step whose segment is the first with tiles has no earlier carrier: its
+// pieces are claimed at run time (an atomic counter) by its own tiles, each
+// of which claims until none are left before it waits.
 //
-// Progress.  A carrier does its chunks without waiting, and a tile of group
-// h waits only for chunks carried by tiles of earlier groups, which precede
-// it in every queue.  Take the lowest group h that any waiting workgroup
-// waits for; every queue that has a waiting workgroup has handed out all its
-// tiles of group h - 1 or earlier (they precede the waiter's tile), and
-// every other queue hands tiles out until it passes them; all of them carry
-// out their chunks.  So every wait ends, given that every queue keeps at
-// least one running workgroup -- two single-launch runs are therefore never
-// in flight together on one device (the host orders them).  A wait is also
-// bounded in time: after the limit it is counted as an error (the run's
-// result is then undefined) and the workgroup goes on without waiting
-// again, so a launch ends within about one limit in any case.
+// Progress.  A carrier does its pieces without waiting, and a tile waits
+// only for pieces carried by tiles of earlier segments, which precede it in
+// every queue, or claimed by tiles that do not wait before finishing them.
+// Take the lowest segment that any waiting workgroup waits for; every queue
+// with a waiting workgroup has handed out all its tiles of earlier segments,
+// and every other queue hands tiles out until it passes them; all of them
+// carry out their pieces.  So every wait ends, given that every queue keeps
+// at least one running workgroup (the host orders single-launch runs on a
+// device one after another).  Should a wait nevertheless outlast its limit
+// (another kernel holding CUs, say), the workgroup copies its strip itself
+// -- the same bytes the carriers write, so the duplicate is harmless, and
+// the strip's region of G is read by no tile that has already finished --
+// counts the event, and goes on with a correct result.
 //
-// Visibility.  Every wave of a carrier waits until its chunk stores have
+// Visibility.  Every wave of a carrier waits until its piece stores have
 // reached L2; after a barrier thread 0 fences at agent scope (L2
-// write-back) and adds the chunks to the group's counter; a waiting thread
-// polls the counter with agent-scope loads and then performs an agent-scope
-// acquire (L1 / L2 invalidate) before the barrier that releases its
-// workgroup into the tile.  All counters are reset by the last workgroup to
-// finish, so every launch starts from zero (also when replayed from a graph).
+// write-back) and adds the pieces to their strips' counters; a waiting
+// thread polls the counter with agent-scope loads and then performs an
+// agent-scope acquire (cache invalidate) before the barrier that releases
+// its workgroup into the tile.  Every piece also counts towards its step, so
+// to keep acquires rare thread 0 reads, after its strip, the step's count
+// once: when the whole step is complete (the usual case, the copies run
+// ahead), the acquire covers every strip of the step and later tiles of the
+// step wait no more; otherwise only the strip is remembered.  The counts
+// are added without waiting for the atomics' return.  All counters are
+// reset by the last workgroup to finish, so every launch starts from zero
+// (also when replayed from a graph).
 #pragma once
 #include "gemm_tile.h"
 
@@ -60,9 +76,11 @@ namespace tile {
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 // Copy `rows` rows of `bytes` bytes (a multiple of sizeof(T)) from src to dst,
-// rows spitch / dpitch bytes apart, with the workgroup's 256 threads; eight
-// units in flight per thread.  Non-temporal: the copied bytes are not reused
-// by this workgroup, and they should not evict the GEMM's operand lines.
+// rows spitch / dpitch bytes apart, with the workgroup's 256 threads: batches
+// of eight units per thread, all eight loads in flight before the stores (the
+// last batch predicated, so a ragged end costs one memory round trip, not
+// one per unit).  Non-temporal: the copied bytes are not reused by this
+// workgroup, and they should not evict the GEMM's operand lines.
 template <typename T>
 __device__ __forceinline__ void copy_rows(const uint8_t* src, int64_t spitch, uint8_t* dst,
                                           int64_t dpitch, int64_t rows, int64_t bytes) {
@@ -72,186 +90,387 @@ __device__ __forceinline__ void copy_rows(const uint8_t* src, int64_t spitch, ui
   if (rows == 1) {
     const T* s = reinterpret_cast<const T*>(src);
     T* d = reinterpret_cast<T*>(dst);
-    int64_t u = tid;
-    for (; u + (U - 1) * kThreads < upr; u += U * kThreads) {
+    for (int64_t u = tid; u < upr; u += U * kThreads) {
       T v[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load(s + u + j * kThreads);
+      for (int j = 0; j < U; ++j)
+        if (u + j * kThreads < upr) v[j] = __builtin_nontemporal_load(s + u + j * kThreads);
 #pragma unroll
-      for (int j = 0; j < U; ++j) __builtin_nontemporal_store(v[j], d + u + j * kThreads);
+      for (int j = 0; j < U; ++j)
+        if (u + j * kThreads < upr) __builtin_nontemporal_store(v[j], d + u + j * kThreads);
     }
-    for (; u < upr; u += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + u), d + u);
     return;
   }
-  // several rows: one flat index over rows x units (a chunk holds < 2^32 units)
+  // several rows: one flat index over rows x units (a piece holds < 2^32 units)
   const uint32_t total = static_cast<uint32_t>(rows * upr);
   const uint32_t up = static_cast<uint32_t>(upr);
-  uint32_t f = tid;
-  for (; f + (U - 1) * kThreads < total; f += U * kThreads) {
+  for (uint32_t f = tid; f < total; f += U * kThreads) {
     T v[U];
-    int64_t so[U], dof[U];
+    int64_t dof[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const uint32_t idx = f + j * kThreads;
       const uint32_t r = idx / up, c = idx - r * up;
-      so[j] = r * spitch + static_cast<int64_t>(c) * sizeof(T);
       dof[j] = r * dpitch + static_cast<int64_t>(c) * sizeof(T);
-      v[j] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + so[j]));
+      if (idx < total)
+        v[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const T*>(src + r * spitch + static_cast<int64_t>(c) * sizeof(T)));
     }
 #pragma unroll
-    for (int j = 0; j < U; ++j) __builtin_nontemporal_store(v[j], reinterpret_cast<T*>(dst + dof[j]));
-  }
-  for (; f < total; f += kThreads) {
-    const uint32_t r = f / up, c = f - r * up;
-    const T v = __builtin_nontemporal_load(
-        reinterpret_cast<const T*>(src + r * spitch + static_cast<int64_t>(c) * sizeof(T)));
-    __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + r * dpitch + static_cast<int64_t>(c) * sizeof(T)));
+    for (int j = 0; j < U; ++j)
+      if (f + j * kThreads < total) __builtin_nontemporal_store(v[j], reinterpret_cast<T*>(dst + dof[j]));
   }
 }
 
-// Chunk c of the copy of group st: shard c / chunks_per_step of the group,
-// and in it row block c' / chunks_per_row, column piece c' mod chunks_per_row
-// (c' = c mod chunks_per_step) of the shard region.
-__device__ __forceinline__ void copy_chunk(const FusedArgs& a, const FusedStep& st, int c) {
-  const int m = c / st.chunks_per_step;  // shard of the group
-  c -= m * st.chunks_per_step;
-  const int64_t pr = c / st.chunks_per_row, pc = c - pr * st.chunks_per_row;
-  const int64_t r0 = pr * st.chunk_rows, c0 = pc * st.chunk_cols;
-  const int64_t rows = min(st.chunk_rows, a.cp_height - r0);
-  const int64_t bytes = min(st.chunk_cols, a.cp_width - c0);
-  const int64_t shard = m * a.cp_width;
-  const uint8_t* src =
-      static_cast<const uint8_t*>(a.copy_src) + st.copy_src_off + shard + r0 * a.cp_src_pitch + c0;
-  uint8_t* dst = a.staging + st.copy_dst_off + shard + r0 * a.cp_dst_pitch + c0;
+// Contiguous copy of `bytes` (a multiple of 16) from src to dst through the
+// workgroup's LDS, which is idle between tiles: each wave streams rounds of
+// 32 KiB straight into its own 32 KiB of LDS (buffer_load ... lds, 32
+// loads of 1 KiB in flight, no registers held while they fly), waits for
+// them, reads them back and stores them (non-temporal).  128 KiB per
+// workgroup in flight: the register-bounded loop above keeps 32 KiB, and
+// at HBM latency that bounds one CU's copy rate.  Loads past the end read
+// zeros (the buffer descriptor covers `bytes`) and are not stored.  The
+// caller passes a barrier before the LDS is used for anything else.
+constexpr int kCopyWaveBytes = 32768;
+__device__ __forceinline__ void copy_lds(const uint8_t* src, uint8_t* dst, int64_t bytes, uint8_t* smem) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  uint8_t* const lbase = smem + wave * kCopyWaveBytes;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, static_cast<uint32_t>(bytes));
+  for (int64_t b0 = 0; b0 < bytes; b0 += 4 * kCopyWaveBytes) {
+    const uint32_t wo = static_cast<uint32_t>(b0) + wave * kCopyWaveBytes + lane * 16;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the last round's reads are done
+#pragma unroll
+    for (int d = 0; d < kCopyWaveBytes / 1024; ++d)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lbase + 1024 * d), 16, wo + 1024 * d, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int d0 = 0; d0 < kCopyWaveBytes / 1024; d0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        v[d] = *reinterpret_cast<const u32x4*>(lbase + 1024 * (d0 + d) + 16 * lane);
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        if (wo + 1024 * (d0 + d) < bytes)
+          __builtin_nontemporal_store(v[d], reinterpret_cast<u32x4*>(dst + wo + 1024 * (d0 + d)));
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Where chunk c of step h lies: strip-list position, batch of G and piece.
+struct ChunkAt {
+  int pos, lg, piece;
+};
+__device__ __forceinline__ ChunkAt chunk_at(const FusedArgs& a, const FusedStepCopy& sh, int c) {
+  const int per_strip = a.LG * sh.P;
+  ChunkAt at;
+  const int sp = c / per_strip;
+  const int rem = c - sp * per_strip;
+  at.pos = sh.strip0 + sp;
+  at.lg = rem / sh.P;
+  at.piece = rem - at.lg * sh.P;
+  return at;
+}
+
+// Copy one piece of strip `strip` of batch lg from the operand into G.
+// Contiguous strips are 256 rows of the operand's storage (A, the N x K
+// storage of B, or C for row chunks); a piece is `piece` bytes of one.
+// Strided strips (C's column chunks) are 256 columns of every row; a piece
+// is `piece` rows of one.  Pieces past the end of a ragged last strip are
+// empty.
+__device__ __forceinline__ void copy_piece(const FusedArgs& a, int64_t piece, int strip, int lg, int pc,
+                                           uint8_t* smem) {
+  const uint8_t* src;
+  uint8_t* dst;
+  int64_t rows, bytes, pitch;
+  const int64_t batch = static_cast<int64_t>(lg) * a.gbatch;
+  if (!a.strided) {
+    const int64_t r0 = static_cast<int64_t>(strip) * kBM;
+    const int64_t r1 = min(r0 + kBM, a.ext);
+    const int64_t off = r0 * a.row_bytes + static_cast<int64_t>(pc) * piece;
+    const int64_t end = r1 * a.row_bytes;
+    if (off >= end) return;
+    bytes = min(piece, end - off);
+    rows = 1;
+    pitch = 0;
+    src = a.src + batch + off;
+    dst = const_cast<uint8_t*>(a.gath) + batch + off;
+    if (a.unit == 16) {
+      copy_lds(src, dst, bytes, smem);
+      return;
+    }
+  } else {
+    const int64_t c0 = static_cast<int64_t>(strip) * kBN;
+    const int64_t c1 = min(c0 + kBN, a.ext);
+    const int64_t rw0 = static_cast<int64_t>(pc) * piece;
+    if (rw0 >= a.height) return;
+    rows = min(piece, a.height - rw0);
+    bytes = (c1 - c0) * a.row_bytes;
+    pitch = a.pitch;
+    const int64_t off = batch + rw0 * a.pitch + c0 * a.row_bytes;
+    src = a.src + off;
+    dst = const_cast<uint8_t*>(a.gath) + off;
+  }
   if (a.unit == 16)
-    copy_rows<u32x4>(src, a.cp_src_pitch, dst, a.cp_dst_pitch, rows, bytes);
+    copy_rows<u32x4>(src, pitch, dst, pitch, rows, bytes);
   else if (a.unit == 4)
-    copy_rows<uint32_t>(src, a.cp_src_pitch, dst, a.cp_dst_pitch, rows, bytes);
+    copy_rows<uint32_t>(src, pitch, dst, pitch, rows, bytes);
   else
-    copy_rows<uint8_t>(src, a.cp_src_pitch, dst, a.cp_dst_pitch, rows, bytes);
+    copy_rows<uint8_t>(src, pitch, dst, pitch, rows, bytes);
 }
 
-// GemmParams of step st for this run's operands.
-__device__ __forceinline__ GemmParams fused_step_params(const FusedArgs& a, const FusedStep& st) {
-  GemmParams g;
-  const uint8_t* stg = a.staging;
-  g.A = (st.stagedA ? stg : static_cast<const uint8_t*>(a.A)) + st.offA;
-  g.B = (st.stagedB ? stg : static_cast<const uint8_t*>(a.B)) + st.offB;
-  g.C = a.beta != 0.0f ? (st.stagedC ? stg : static_cast<const uint8_t*>(a.C)) + st.offC : nullptr;
-  g.D = static_cast<uint8_t*>(a.D) + st.offD;
-  g.bias = a.bias ? static_cast<const uint8_t*>(a.bias) + st.offBias : nullptr;
-  g.lda = st.lda; g.ldb = st.ldb; g.ldc = st.ldc; g.ldd = st.ldd;
-  g.sA = st.sA; g.sB = st.sB; g.sC = st.sC; g.sD = st.sD;
-  g.M = st.M; g.N = st.N; g.K = a.K; g.L = a.L;
-  g.alpha = a.alpha; g.beta = a.beta;
-  return g;
+__device__ __forceinline__ uint32_t* strip_counter(const FusedArgs& a, int lg, int strip) {
+  return a.ctr + static_cast<int64_t>(lg) * a.n_strips + strip;
+}
+// pieces done of step h in batch lg (after the strip counters)
+__device__ __forceinline__ uint32_t* step_counter(const FusedArgs& a, int lg, int h) {
+  return a.ctr + static_cast<int64_t>(a.LG) * a.n_strips + static_cast<int64_t>(lg) * a.S + h;
+}
+
+// Thread 0: the finished chunks of this workgroup are in L2 (every wave
+// waited for its stores and passed a barrier): count them, towards their
+// strip and their step (no atomic's return is waited for).
+__device__ __forceinline__ void count_chunk(const FusedArgs& a, int h, int c) {
+  const FusedStepCopy& sh = a.steps[h];
+  const ChunkAt at = chunk_at(a, sh, c);
+  const int strip = a.strip_list[at.pos];
+  __hip_atomic_fetch_add(strip_counter(a, at.lg, strip), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(step_counter(a, at.lg, h), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the step's copy time: the latest stamp of any of its pieces
+  if (a.times)
+    __hip_atomic_fetch_max(a.times + 1 + 3 * h, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Rank of item i of queue q among all items of a segment (T2 tiles per
+// batch, L batches, nq queues) in the order they start: by position in their
+// queue first, then by queue.  Queue q' holds n(q') = (T2/nq + (q' < T2 mod
+// nq)) * L items, so the rank is the number of items (i', q') with i' < i,
+// plus the queues before q that still have an item at position i.
+__device__ __forceinline__ int64_t item_rank(int i, int q, int T2, int L, int nq) {
+  const int qq = T2 / nq, r = T2 - qq * nq;
+  const int nA = (qq + 1) * L, nB = qq * L;
+  const int64_t before = static_cast<int64_t>(r) * min(i, nA) + static_cast<int64_t>(nq - r) * min(i, nB);
+  const int same = (nA > i ? min(q, r) : 0) + (nB > i ? max(0, q - r) : 0);
+  return before + same;
 }
 
 template <int IN, int OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 fused_run_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * kOperandSlab];
-  // item broadcast word: at the end of the last ring slot, which a tile first
-  // fills only after its prologue barrier (by then every wave has read the
-  // word) and which the epilogue leaves alone
+  // broadcast words: at the end of the last ring slot, which a tile first
+  // fills only after its prologue barrier (by then every wave has read them)
+  // and which the epilogue leaves alone
   volatile int32_t* bcast = reinterpret_cast<volatile int32_t*>(smem + kSlots * kOperandSlab - 256);
   const int tid = threadIdx.x;
-  const int S = a.S;
   const int q = static_cast<int>(blockIdx.x) % a.nq;
   int32_t* const qctr = a.sync + q * kSyncStride;
-  int32_t* const done = a.sync + kSyncDone * kSyncStride;
   int32_t* const nexit = a.sync + kSyncExit * kSyncStride;
   int32_t* const nerr = a.sync + kSyncErr * kSyncStride;
-  const int32_t* const seg = a.seg + q * (S + 1);
-  const int n_items = seg[S];
+  const int32_t* const seg = a.seg + q * (a.n_seg + 1);
+  const int n_items = seg[a.n_seg];
+  const uint64_t t_start = wall_clock64();
+  if (a.times && tid == 0)
+    __hip_atomic_fetch_max(a.times, ~t_start, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  uint64_t ready = 0;     // thread 0: groups < 64 seen complete
-  bool gave_up = false;   // thread 0: a wait ran out; wait no more in this launch
-  int g = 0;              // group of the last tile (tiles come in increasing order)
+  // thread 0, for batch acq_l: the steps (bit h, h < 64) and the strips of
+  // segment acq_g (bit p: segment position p < 64) seen complete before an
+  // acquire
+  int acq_g = -1, acq_l = -1;
+  uint64_t acq_steps = 0, acq_strips = 0;
+  bool delayed = a.delay == 0;
+  int g = 0;  // segment of the last tile (tiles come in increasing order)
   for (;;) {
-    barrier_only();  // every wave is done with the previous tile
+    barrier_only();  // every wave is done with the previous tile and its broadcast words
     if (tid == 0) bcast[0] = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_only();
     const int k = __builtin_amdgcn_readfirstlane(bcast[0]);
     if (k >= n_items) break;
     while (k >= seg[g + 1]) ++g;
-    const FusedStep& st = a.steps[g];
-    // the tile: position i of this queue's share of group g
+    const FusedSeg& sg = a.segs[g];
+    // the tile: position i of this queue's share of segment g
     const int i = k - seg[g];
-    const int T2 = st.tiles_m * st.tiles_n;
+    const int T2 = sg.tiles;
     const int qq = T2 / a.nq, r = T2 - qq * a.nq;
     const int share = qq + (q < r ? 1 : 0), first = q * qq + min(q, r);
     const int l = i / share, j = i - l * share;
-    const int gidx = l * T2 + first + j;  // index among all tiles of the group
-    const int gtiles = T2 * a.L;
+    const int gtiles = T2 * a.g.L;
+    // the segment's tile order: groups of four tile rows walked column by
+    // column, as the monolithic kernel walks (row strips: the rows are the
+    // strips; column strips: the strips are the columns)
+    int sp, ob;
+    if (a.cols)
+      order_tile(first + j, T2 / sg.nst, sg.nst, ob, sp);
+    else
+      order_tile(first + j, sg.nst, T2 / sg.nst, sp, ob);
+    const int pos = sg.strip0 + sp;
+    const int strip = a.strip_list[pos];
+    const int h_own = a.strip_step[pos];
+    const FusedStepCopy& own = a.steps[h_own];
+    const bool wait = a.copy_on && own.wait;
+    const int lg = a.LG == 1 ? 0 : l;
+    // steps whose chunks this tile carries or claims (none when nothing rotates)
+    const int carry0 = a.copy_on ? (sg.carry_first == 0 && !a.copy_local ? 1 : sg.carry_first) : 1;
+    const int carry1 = a.copy_on ? sg.carry_last : 0;
+    const int claim0 = a.copy_on ? sg.claim_first : 1;
+    const int claim1 = a.copy_on ? sg.claim_last : 0;
 
-    // 1. the chunks this tile carries: chunk gidx, gidx + gtiles, ... of the
-    //    copy of every group the tiles of group g carry
-    const int h0 = g == 0 ? 1 : g + a.ahead;
-    const int h1 = min(S - 1, g == 0 ? a.ahead : g + a.ahead);
-    bool copied = false;
-    for (int h = h0; h <= h1; ++h) {
-      const FusedStep& sh = a.steps[h];
-      for (int c = gidx; c < sh.n_chunks; c += gtiles) {
-        copy_chunk(a, sh, c);
-        copied = true;
+    // 1. the chunks this tile carries: the segment carries the steps
+    //    carry0..carry1, whose chunks form one list in step order; the
+    //    segment's tiles, ranked by the order in which they start, take
+    //    balanced contiguous ranges of it, so the earliest steps' copies are
+    //    done first.  Then, for a step without an earlier carrier, chunks
+    //    claimed until none are left.
+    if (!delayed && (carry0 <= carry1 || claim0 <= claim1)) {
+      if (tid == 0)
+        while (wall_clock64() - t_start < static_cast<uint64_t>(a.delay)) __builtin_amdgcn_s_sleep(8);
+      delayed = true;
+      barrier_only();
+    }
+    if (carry0 <= carry1) {
+      int64_t n = 0;
+      for (int h = carry0; h <= carry1; ++h) n += a.steps[h].n_chunks;
+      const int64_t rank = item_rank(i, q, T2, a.g.L, a.nq);
+      const int64_t p0 = rank * n / gtiles, p1 = (rank + 1) * n / gtiles;
+      if (p0 < p1) {
+        int h = carry0;
+        int64_t base = 0;
+        for (int64_t p = p0; p < p1; ++p) {
+          while (p - base >= a.steps[h].n_chunks) base += a.steps[h++].n_chunks;
+          const FusedStepCopy& sh = a.steps[h];
+          const ChunkAt at = chunk_at(a, sh, static_cast<int>(p - base));
+          copy_piece(a, sh.piece, a.strip_list[at.pos], at.lg, at.piece, smem);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are in L2
+        barrier_only();
+        if (tid == 0) {
+          __threadfence();  // write back the chunks, then count them
+          h = carry0;
+          base = 0;
+          for (int64_t p = p0; p < p1; ++p) {
+            while (p - base >= a.steps[h].n_chunks) base += a.steps[h++].n_chunks;
+            count_chunk(a, h, static_cast<int>(p - base));
+          }
+        }
       }
     }
-    if (copied) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are in L2
-      barrier_only();
-      if (tid == 0) {
-        __threadfence();  // write back the chunks, then count them
-        for (int h = h0; h <= h1; ++h) {
-          const int n = a.steps[h].n_chunks;
-          const int cnt = gidx < n ? (n - gidx + gtiles - 1) / gtiles : 0;
-          if (cnt > 0)
-            __hip_atomic_fetch_add(done + h * kSyncStride, cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int h = claim0; h <= claim1; ++h) {
+      const FusedStepCopy& sh = a.steps[h];
+      int32_t* const claim = a.sync + (kSyncClaim + h) * kSyncStride;
+      for (;;) {
+        barrier_only();
+        if (tid == 0) bcast[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        barrier_only();
+        const int c = __builtin_amdgcn_readfirstlane(bcast[1]);
+        if (c >= sh.n_chunks) break;
+        const ChunkAt at = chunk_at(a, sh, c);
+        copy_piece(a, sh.piece, a.strip_list[at.pos], at.lg, at.piece, smem);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier_only();
+        if (tid == 0) {
+          __threadfence();
+          count_chunk(a, h, c);
         }
       }
     }
 
-    // 2. a staged group's tile waits until the group's copy is complete
-    if (st.n_chunks > 0) {
+    // 2. a tile of a staged strip waits until the strip is complete
+    if (wait) {
       if (tid == 0) {
-        const bool known = g < 64 && ((ready >> g) & 1);
-        if (!known && !gave_up) {
+        int gave_up = 0;
+        if (acq_l != lg) {
+          acq_l = lg;
+          acq_steps = 0;
+          acq_g = -1;
+        }
+        if (acq_g != g) {
+          acq_g = g;
+          acq_strips = 0;
+        }
+        const bool known = (h_own < 64 && ((acq_steps >> h_own) & 1)) || (sp < 64 && ((acq_strips >> sp) & 1));
+        if (!known) {
+          const uint32_t P = static_cast<uint32_t>(own.P);
+          uint32_t* const ctr = strip_counter(a, lg, strip);
           const uint64_t t0 = wall_clock64();
-          while (__hip_atomic_load(done + g * kSyncStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                 st.n_chunks) {
+          while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < P) {
             if (wall_clock64() - t0 > static_cast<uint64_t>(a.spin_limit)) {
               __hip_atomic_fetch_add(nerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              gave_up = true;
+              gave_up = 1;
               break;
             }
             __builtin_amdgcn_s_sleep(1);
           }
+          if (!gave_up) {
+            // the whole step complete?  then the acquire below covers all of it
+            const uint32_t v = __hip_atomic_load(step_counter(a, lg, h_own), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            if (h_own < 64 && v >= P * static_cast<uint32_t>(own.nst))
+              acq_steps |= 1ull << h_own;
+            else if (sp < 64)
+              acq_strips |= 1ull << sp;
+          }
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          if (g < 64) ready |= 1ull << g;
         }
+        bcast[2] = gave_up;
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       barrier_only();
+      if (__builtin_amdgcn_readfirstlane(bcast[2])) {
+        // the wait ran out: copy the strip here (the carriers' bytes exactly)
+        const int per = own.P;
+        for (int pc = 0; pc < per; ++pc) copy_piece(a, own.piece, strip, lg, pc, smem);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier_only();
+        if (tid == 0) {
+          __threadfence();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        barrier_only();
+      }
     }
 
-    // 3. the GEMM tile
-    int tm, tn;
-    order_tile(first + j, st.tiles_m, st.tiles_n, tm, tn);
-    const GemmParams gp = fused_step_params(a, st);
+    // 3. the GEMM tile, the rotating operand read from G for a staged strip
+    if (a.times && tid == 0)
+      __hip_atomic_fetch_max(a.times + 2 + 3 * h_own, ~wall_clock64(), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    GemmParams gp = a.g;
+    if (wait) {
+      if (a.rot == 0) gp.A = a.gath;
+      else if (a.rot == 1) gp.B = a.gath;
+      else gp.C = a.gath;
+    }
+    const int tm = a.cols ? ob : strip;
+    const int tn = a.cols ? strip : ob;
     gemm_tile<IN, OUT>(gp, l, tm, tn, smem);
+    if (a.times && tid == 0)
+      __hip_atomic_fetch_max(a.times + 3 + 3 * h_own, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
     __threadfence();
     const int old = __hip_atomic_fetch_add(nexit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == static_cast<int>(gridDim.x) - 1) {
+    bcast[3] = old == static_cast<int>(gridDim.x) - 1;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier_only();
+  if (bcast[3]) {
+    const int n = a.LG * (a.n_strips + a.S);
+    for (int x = tid; x < n; x += kThreads)
+      __hip_atomic_store(a.ctr + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
       for (int x = 0; x < a.nq; ++x)
         __hip_atomic_store(a.sync + x * kSyncStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int s = 0; s < S; ++s)
-        __hip_atomic_store(done + s * kSyncStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int h = 0; h < a.S; ++h)
+        __hip_atomic_store(a.sync + (kSyncClaim + h) * kSyncStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(nexit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
     }
+    if (a.times_next)
+      for (int x = tid; x < 1 + 3 * a.S; x += kThreads) a.times_next[x] = 0;
+    __threadfence();
   }
 }
 

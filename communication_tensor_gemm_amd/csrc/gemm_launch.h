@@ -33,66 +33,93 @@ constexpr int kRowBytes = 128;
 inline int in_elem_size(int in_kind) { return in_kind == IN_F32 ? 4 : (in_kind == IN_BF16 ? 2 : 1); }
 inline int out_elem_size(int out_kind) { return out_kind == OUT_F32 ? 4 : 2; }
 
-// ---- Single-launch run: device-side step flags --------------------------
+// ---- Single-launch run: device-side strip readiness -----------------------
 //
-// One persistent launch computes every step of a run and performs the shard
-// rotation itself.  Its work items are tiles; workgroup b takes them from
-// queue b mod nq, in queue order (queue q: its tiles of launch group 0, then
-// of group 1, ...), by an atomic counter.  The copy of group h is cut into
-// chunks carried by the tiles of group max(0, h - ahead), which copy them
-// before their own GEMM; a tile of a staged group waits until every chunk of
-// its group's copy is done.  Pointers are not stored: offsets are relative
-// to the run's operands.
+// One persistent launch computes every step of a run on the monolithic tile
+// grid and performs the shard rotation itself.  The rotating operand (A, B
+// or the partial C) is gathered into an image G with the operand's own
+// layout; a tile that reads a staged shard reads G.  Readiness is kept per
+// strip: the 256 rows (row schedules) or 256 columns (column schedules) of
+// the rotating operand that one tile row / column reads.  A strip's step is
+// the latest step (in rotation order) of the shards it overlaps; the strips
+// of step 0 lie inside the local shard and are read in place.
+//
+// Work items are the tiles.  Workgroup b takes them from queue b mod nq, in
+// queue order, by an atomic counter; the queue order is by segment (step 0,
+// then groups of consecutive staged steps), each segment's tiles split into
+// nq contiguous ranges of its tile order.  The copy of step h is cut into
+// chunks (pieces of its strips) carried by the tiles of an earlier segment,
+// which copy them before their own GEMM; a tile of a staged strip waits
+// until every piece of that strip is done.  Pointers are not stored in the
+// tables; per-run pointers travel in FusedArgs.
 
-// One launch group of steps (consecutive steps on adjacent shards, computed
-// as one GEMM over their union), pointer-free: its GemmParams without the
-// base pointers, and its copy: count consecutive shards, chunks_per_step
-// chunks each (shard m of the group at + m * cp_width bytes in both the
-// rotating operand and the staging rows); a chunk is chunk_rows rows x
-// chunk_cols bytes of the shard region, chunks_per_row pieces per row block.
-struct FusedStep {
-  int64_t offA, offB, offC, offD;  // bytes from the operand base (A / B / C / D or staging)
-  int64_t lda, ldb, ldc, ldd;      // elements
-  int64_t sA, sB, sC, sD;          // batch strides, elements
-  int64_t offBias;                 // bytes: the group's first column in the bias vector
-  int64_t copy_src_off;            // bytes: the group's first shard in the rotating operand
-  int64_t copy_dst_off;            // bytes: its staging slot
-  int64_t chunk_cols, chunk_rows;
-  int32_t chunks_per_row, chunks_per_step;
-  int32_t M, N, tiles_m, tiles_n;
-  int32_t stagedA, stagedB, stagedC;  // operand read from the staging buffer
-  int32_t n_chunks;                   // chunks of the group's copy (0: not staged)
+// One queue segment: consecutive steps whose tiles are ordered together.
+struct FusedSeg {
+  int32_t strip0, nst;               // its strips: positions strip0 .. strip0 + nst - 1
+  int32_t tiles;                     // tiles of one batch: nst * other_tiles
+  int32_t carry_first, carry_last;   // steps whose chunks its tiles carry (first > last: none)
+  int32_t claim_first, claim_last;   // steps whose chunks its tiles claim at run time
+};
+
+// The copy of one step: its strips and their pieces.
+struct FusedStepCopy {
+  int64_t piece;        // bytes (row strips) or rows (column strips) per piece
+  int32_t strip0, nst;  // its strips: positions in the strip list
+  int32_t P;            // pieces per strip (the target of each strip's counter)
+  int32_t n_chunks;     // nst * LG * P when the step's strips are copied, else 0
+  int32_t wait;         // its tiles wait for their strip and read the gathered image
+  int32_t pad;
 };
 
 // Synchronisation words (int32, one 128-byte line each), zero between runs
 // except the error count:
 //   [q] queue counters, q < nq;  [kSyncExit] workgroups finished;
 //   [kSyncErr] timed-out waits (never reset by a run);
-//   [kSyncDone + g] chunks done of launch group g.
+//   [kSyncClaim + h] chunks of step h claimed at run time.
 constexpr int kSyncStride = 32;
 constexpr int kMaxQueues = 8;
 constexpr int kSyncExit = kMaxQueues;
 constexpr int kSyncErr = kMaxQueues + 1;
-constexpr int kSyncDone = kMaxQueues + 2;
+constexpr int kSyncClaim = kMaxQueues + 2;
+inline int sync_words(int S) { return (kSyncClaim + S) * kSyncStride; }
+
+// Device timeline of one run (unsigned 64-bit wall-clock ticks), written
+// with atomic max only: [0] = ~(first workgroup start); per step s,
+// [1 + 3s] = last piece of the step's copy counted, [2 + 3s] = ~(first
+// tile of the step begins), [3 + 3s] = last tile of the step ends.  Zero
+// at the start of the run (the previous launch zeroes it at its end).
+inline int timeline_words(int S) { return 1 + 3 * S; }
 
 struct FusedArgs {
-  const void* A;
-  const void* B;
-  const void* C;           // NULL when beta == 0 (unless it is the rotating operand)
-  void* D;
-  const void* bias;        // NULL or N values of the output type
-  uint8_t* staging;
-  const void* copy_src;    // the rotating operand (A, B or C)
-  const FusedStep* steps;  // [S] launch groups
-  const int32_t* seg;      // [nq][S + 1]: first tile of group g in queue q; [q][S] = tiles
+  GemmParams g;                  // the whole problem on the monolithic tile grid
+  const uint8_t* gath;           // G: the gathered image of the rotating operand
+  const uint8_t* src;            // the rotating operand (source of the copies)
+  const FusedSeg* segs;          // [n_seg]
+  const FusedStepCopy* steps;    // [S]
+  const int32_t* strip_list;     // strips, step by step
+  const int32_t* strip_step;     // step of each strip-list position
+  const int32_t* seg;            // [nq][n_seg + 1]: first item of segment g in queue q
   int32_t* sync;
-  int64_t cp_width, cp_height;         // shard region: height rows of cp_width bytes
-  int64_t cp_src_pitch, cp_dst_pitch;  // bytes between rows
-  int64_t spin_limit;                  // wall-clock ticks a wait may last
-  int32_t unit;                        // copy unit: 16, 4 or 1 bytes
-  int32_t S, K, L, nq;  // S: number of launch groups
-  int32_t ahead;        // copy lookahead D >= 1 (in launch groups)
-  float alpha, beta;
+  uint32_t* ctr;                 // [LG][n_strips] pieces done per strip, then [LG][S] per
+                                 // step; zero between runs
+  uint64_t* times;               // NULL, or this run's timeline (zero at the start)
+  uint64_t* times_next;          // NULL, or the next run's timeline, zeroed at the end
+  int64_t row_bytes;             // contiguous strips: bytes per row of the operand; strided: element bytes
+  int64_t ext;                   // rows or columns of the operand along the strip dimension
+  int64_t gbatch;                // bytes between batches of the operand and of G
+  int64_t pitch;                 // strided strips: bytes between rows
+  int64_t height;                // strided strips: rows per batch
+  int64_t spin_limit;            // wall-clock ticks a wait may last
+  int64_t delay;                 // ticks a workgroup waits before its first copy (0: none)
+  int32_t rot;                   // rotating operand: 0 A, 1 B, 2 C
+  int32_t cols;                  // 1: strips are tile columns
+  int32_t strided;               // 1: a strip is 256 columns of every row (else contiguous rows)
+  int32_t n_strips;              // strips per batch
+  int32_t LG;                    // batches of G (1 when A is shared)
+  int32_t unit;                  // copy unit: 16, 4 or 1 bytes
+  int32_t n_seg, nq, S;
+  int32_t copy_on;               // 0: nothing rotates (a reduce-scatter with beta = 0)
+  int32_t copy_local;            // 1: step 0's strips are copied into G too (G is returned)
 };
 
 // Enqueue the single-launch run on `stream` with `grid` workgroups (a

@@ -15,13 +15,15 @@
  * engine while the GEMM of the previous step runs, and each step's GEMM
  * waits for its operand before it starts.  On one GPU the peer's shard is a
  * region of the caller's full operand; the library copies it device to
- * device into a plan-owned staging slot, and the step GEMM reads it from
- * there.  By default one persistent kernel per run does both: its
- * workgroups copy the shards in chunks ahead of use and compute the step
- * tiles, each staged step's tiles starting once a device-side counter shows
- * the step's shard complete (DIST_GEMM_OPT_EXECUTION = 1).  The alternative
- * (= 0) launches the step GEMMs separately and copies on side streams,
- * ordered by events.
+ * device into the same region of a gathered image of that operand (the
+ * plan's, or the caller's gathered output, see dist_gemm_run_ag), and the
+ * step GEMM reads it from there.  By default one persistent kernel per run
+ * does both: its workgroups copy the shards in pieces ahead of use and
+ * compute the tiles of the monolithic tile grid, a tile that reads a staged
+ * shard starting once a device-side counter shows the 256 rows (or columns)
+ * of the gathered operand that it reads complete (DIST_GEMM_OPT_EXECUTION =
+ * 1).  The alternative (= 0) launches the step GEMMs separately and copies
+ * on side streams, ordered by events.
  *
  * Layouts (all row-major, element strides, batch index outermost):
  *   A : L x M x K   (K contiguous, lda = K, batch stride M*K)
@@ -105,8 +107,9 @@ enum dist_gemm_dtype {
 typedef struct dist_gemm_step {
   int32_t step;     /* s */
   int32_t shard;    /* shard / chunk index j */
-  int32_t staged;   /* 1: operand arrives by a copy into a staging slot */
-  int32_t slot;     /* staging slot index (-1 when not staged) */
+  int32_t staged;   /* 1: operand arrives by a copy into the gathered image */
+  int32_t slot;     /* position of that copy in the gathered image, in shards
+                       (= shard; -1 when not staged) */
   int64_t m0, m1;   /* row range of D written by this step */
   int64_t n0, n1;   /* column range of D written by this step */
 } dist_gemm_step;
@@ -122,10 +125,12 @@ int dist_gemm_step_table(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int
                          int dtype, dist_gemm_step* out, int* n_steps);
 
 /* Create a plan on the current HIP device: validates the problem (same
- * rules as dist_gemm_step_table), builds the step table, allocates
- * (TP-1) staging slots of one shard each (none for MONOLITHIC or TP = 1),
- * one side stream for copies, one second compute stream, and the events
- * that order them.  *out receives the handle (NULL on failure). */
+ * rules as dist_gemm_step_table), builds the step table, allocates the
+ * gathered image of the rotating operand (A for AG_ROT_A, B for AG_ROT_B,
+ * C for the reduce-scatter schedules; L batches, same layout as the
+ * operand; none for MONOLITHIC or TP = 1), the single-launch tables and
+ * counters, one side stream for copies, one second compute stream, and the
+ * events that order them.  *out receives the handle (NULL on failure). */
 int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
                    dist_gemm_plan_t* out);
 
@@ -174,49 +179,70 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     concurrently; n copy streams stand in for n such links.  Default 2
  *     (with the two compute streams, four streams: the hardware queues a
  *     process gets by default).
- *   DIST_GEMM_OPT_STEP_GROUP: g in 1..1024 = at most g consecutive staged
- *     steps run as one GEMM (one launch in mode 0, one group of tiles in
- *     mode 1) once all of their shards have arrived.
- *     Consecutive steps consume adjacent shards (rows of A, columns of B or
- *     of the partial) that sit in adjacent staging slots, so their GEMMs
- *     are one GEMM over the union; every output element is computed exactly
- *     as by its own step.  The step that uses the local shard launches
- *     alone.  1 = one launch per step; default 2.
+ *   DIST_GEMM_OPT_STEP_GROUP: g in 1..1024.  Mode 0: at most g consecutive
+ *     staged steps run as one GEMM launch once all of their shards have
+ *     arrived.  Consecutive steps consume adjacent shards (rows of A,
+ *     columns of B or of the partial) that sit side by side in the gathered
+ *     image, so their GEMMs are one GEMM over the union; every output
+ *     element is computed exactly as by its own step.  The step that uses
+ *     the local shard launches alone.  Mode 1: the tiles of g consecutive
+ *     staged steps form one queue segment, ordered and split over the work
+ *     queues together.  1 = one launch / segment per step; default 2.
  *   DIST_GEMM_OPT_EXECUTION: how a run with more than one step executes.
  *     0 = step launches and side-stream copies (the options above apply);
  *     1 (default) = one persistent launch on the caller's stream does
- *     the whole run: its workgroups compute the step tiles, every tile
- *     first copying an equal chunk of a later step's shard, and a tile of a
- *     staged step starts once a device-side counter shows its step's shard
- *     complete (the per-step ready barrier of the Distributed GEMM
- *     pull-request page, kept on the device).  Every element is computed exactly as in mode 0 (same
- *     kernel tile, same K order).  Single-launch runs on one device are
- *     ordered after one another, also across plans (their workgroups must
- *     not wait on each other), except inside a graph capture.
+ *     the whole run on the monolithic tile grid: its workgroups take the
+ *     tiles step by step, every tile first copying an equal piece of a
+ *     later step's shard, and a tile that reads a staged shard starts once
+ *     a device-side counter shows complete the strip it reads -- the 256
+ *     rows (AG_ROT_A, RS_TILE_A_ROT_C) or columns (AG_ROT_B,
+ *     RS_TILE_B_ROT_C) of the gathered operand that one tile row or column
+ *     uses (the per-step ready barrier of the Distributed GEMM pull-request
+ *     page, kept on the device per tile row or column; a strip that
+ *     straddles two shards waits for both).  Every element is computed
+ *     exactly as by the monolithic GEMM and by mode 0 (same kernel tile,
+ *     same K order).  Single-launch runs on one device are ordered after
+ *     one another, also across plans (their workgroups should not wait on
+ *     each other), except inside a graph capture.
  *   DIST_GEMM_OPT_QUEUES (mode 1): 8 (default) = one work queue per XCD,
  *     each XCD runs contiguous ranges of every step's tile order; 1 = one
  *     queue for the chip.
- *   DIST_GEMM_OPT_COPY_CHUNK (mode 1): the largest copy chunk one tile
+ *   DIST_GEMM_OPT_COPY_CHUNK (mode 1): the largest copy piece one tile
  *     carries, in bytes, a multiple of 16 in [4096, 2^28]; default 2 MiB.
- *     A step's shard is spread over the tiles of the group D before it in
- *     chunks of about equal size (shard bytes / tiles), capped by this.  The plan's device tables are
- *     rebuilt (synchronously) when it changes.
- *   DIST_GEMM_OPT_WAIT_LIMIT_US (mode 1): how long one wait for a shard may
- *     last, in microseconds, in [0, 10^8]; default 10^6.  A wait that runs
- *     out is counted (dist_gemm_device_errors) and the tile proceeds with
- *     whatever the staging slot holds: the run's result is then undefined.
- *     In correct operation no wait runs out.
- *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 1..64; the chunks of launch
- *     group h are carried by the tiles of group max(0, h - D), i.e. D
- *     groups ahead of their use; default 4 (measured 0.5-2% faster than 2
- *     on the TP=8 workloads, where it puts every copy on the first group).
+ *     A step's strips are spread over the tiles of the segment D before it
+ *     in pieces of about equal size (step bytes / carrier tiles), capped by
+ *     this.  The plan's device tables are rebuilt (synchronously) when it
+ *     changes.
+ *   DIST_GEMM_OPT_WAIT_LIMIT_US (mode 1): how long one wait for a strip
+ *     may last, in microseconds, in [0, 10^8]; default 10^6.  A wait that
+ *     runs out is counted (dist_gemm_device_errors) and the waiting
+ *     workgroup copies the strip into the gathered image itself (the same
+ *     bytes its carriers write), so the result stays correct; it only costs
+ *     time.  Waits run out when the launch cannot keep a workgroup running
+ *     on every work queue (other kernels holding the device's CUs), never
+ *     in an unshared device; 0 makes every wait copy its own strip.
+ *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 1..64; the pieces of a step in
+ *     segment h are carried by the tiles of the latest segment at or before
+ *     h - D that has tiles (else the first segment that has), i.e. about D
+ *     segments ahead of their use; default 4 (measured 0.5-2% faster than 2
+ *     on the TP=8 workloads, where it puts every copy on step 0's tiles).
  *   DIST_GEMM_OPT_SHARED_A: 1 = A holds one M x K matrix that every one of
  *     the L batches multiplies (B, C, D keep their L batches): the several-B
  *     form of the PyTorch symmetric-memory page's fused all-gather matmul
  *     (one gathered A, one output per B, e.g. the gate and up projections).
  *     With AG_ROT_A the A shards are rotated once for all L products.
  *     0 (default) = A has L batches like the other operands.  Waits for the
- *     plan's last run when it changes. */
+ *     plan's last run when it changes.
+ *   DIST_GEMM_OPT_COPY_DELAY_US: a test hook that holds back every shard
+ *     copy by this many microseconds, in [0, 10^6] (default 0): in mode 1
+ *     each workgroup starts its first copy piece no earlier than this long
+ *     after it started; in mode 0 each side stream first runs a one-thread
+ *     kernel that waits this long.  The consumers must wait for the late
+ *     copies, so a run with a delay must equal the run without bit for bit.
+ * Options that rebuild the single-launch tables (QUEUES, COPY_CHUNK,
+ * COPY_AHEAD, STEP_GROUP, SHARED_A) return UNSUPPORTED, and leave the plan
+ * unchanged, once a run of the plan has been captured into a graph: the
+ * graph's kernel arguments hold the tables' sizes. */
 enum dist_gemm_option {
   DIST_GEMM_OPT_COMPUTE_STREAMS = 0,
   DIST_GEMM_OPT_COPY_ENGINE = 1,
@@ -228,7 +254,8 @@ enum dist_gemm_option {
   DIST_GEMM_OPT_COPY_CHUNK = 7,
   DIST_GEMM_OPT_WAIT_LIMIT_US = 8,
   DIST_GEMM_OPT_COPY_AHEAD = 9,
-  DIST_GEMM_OPT_SHARED_A = 10
+  DIST_GEMM_OPT_SHARED_A = 10,
+  DIST_GEMM_OPT_COPY_DELAY_US = 11
 };
 int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
 
@@ -236,9 +263,10 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  * null stream) and return without waiting.  Completion of every step, copy
  * and side-stream operation is ordered before any later work on `stream`.
  *   A, B, D: required device pointers.  C: may be NULL iff beta == 0 (C is
- *   not read when beta == 0).  D may alias C exactly (same pointer) for the
- *   RS schedules and MONOLITHIC; no other overlap between D and A, B or C is
- *   allowed.  A and B are only read.
+ *   not read when beta == 0; a reduce-scatter schedule with beta == 0 then
+ *   has no partial to rotate and copies nothing).  D may alias C exactly
+ *   (same pointer) for the RS schedules and MONOLITHIC; no other overlap
+ *   between D and A, B or C is allowed.  A and B are only read.
  * Buffers must stay allocated until the work completes on `stream`.  A run
  * on another stream first waits for the plan's previous run.
  * A reduce-scatter that averages over the ranks (the reduce_op "avg" of the
@@ -259,11 +287,29 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
  * `stream` (a single-launch run: one kernel launch), so it can be captured
  * into a HIP graph.  A captured single-launch run is not ordered against
  * single-launch runs of other plans: do not replay it while one of those
- * may run on the device.  The graph uses the
- * plan's staging buffer: its replays must not overlap other runs of the
- * plan, and the plan must outlive the graph. */
+ * may run on the device (a wait that then runs out costs time, not
+ * correctness; see DIST_GEMM_OPT_WAIT_LIMIT_US).  The graph uses the plan's
+ * gathered image and device tables: its replays must not overlap other
+ * runs of the plan, the plan must outlive the graph, and once captured the
+ * plan refuses the options that rebuild its tables. */
 int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
                   float alpha, float beta, void* stream);
+
+/* dist_gemm_run that also returns the gathered operand (the fused
+ * all-gather matmul of the PyTorch symmetric-memory page returns the
+ * all-gathered A beside the products): for AG_ROT_A, `ag_out` receives A
+ * (L x M x K, or M x K with DIST_GEMM_OPT_SHARED_A) and for AG_ROT_B it
+ * receives B (L x N x K), in the operand's layout.  `ag_out` replaces the
+ * plan's gathered image for this run: every staged shard is copied into
+ * it and the steps that consume a copied shard read it from there, and the
+ * local shard is copied into it too, so on completion it equals the
+ * operand bit for bit.  The caller owns `ag_out` (device memory on the
+ * plan's device, not overlapping A, B, C or D) and keeps it allocated until
+ * the run completes on `stream`.  INVALID_ARG for a NULL `ag_out` or a
+ * reduce-scatter or MONOLITHIC plan (nothing is gathered there); otherwise
+ * as dist_gemm_run. */
+int dist_gemm_run_ag(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
+                     void* ag_out, float alpha, float beta, void* stream);
 
 /* Query the plan's step table (same contents as dist_gemm_step_table). */
 int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_steps);
@@ -278,17 +324,23 @@ int dist_gemm_step_times(dist_gemm_plan_t plan, float* ms, int* n);
 /* With DIST_GEMM_OPT_STEP_TIMING set: wait for the last run to finish and
  * write its timeline, three values per step in step order, in milliseconds
  * since the run was enqueued on its stream: [3s] = the moment the step's
- * shard copy completed (-1 for a step that consumes no copy, and for every
- * step of a single-launch run, whose copies happen inside the launch),
- * [3s+1] = the GEMM launch that computed it began, [3s+2] = it ended.  At
- * most *n values are written; *n receives 3 * steps.  UNSUPPORTED if no timed run exists. */
+ * shard copy completed (-1 for a step that consumes no copy), [3s+1] = the
+ * GEMM work of the step began, [3s+2] = it ended.  Step launches (mode 0):
+ * event times of the copy and of the launch that computed the step.  One
+ * launch (mode 1): the device's own wall-clock stamps -- the last strip of
+ * the step complete, the first tile of the step starting after its wait,
+ * the last tile of the step done -- placed on the run's time line by the
+ * launch's start event (-1 where a step has no copy or no tile of its own:
+ * strips that straddle two shards count for the later step).  At most *n
+ * values are written; *n receives 3 * steps.  UNSUPPORTED if no timed run
+ * exists. */
 int dist_gemm_step_timeline(dist_gemm_plan_t plan, float* ms, int* n);
 
 /* Wait for the plan's last run and write to *count the number of device-side
- * shard waits that ran out of time (DIST_GEMM_OPT_WAIT_LIMIT_US) in all
- * single-launch runs of the plan so far.  0 in correct operation; a run with
- * a wait that ran out has an undefined result.  INVALID_ARG for NULL
- * arguments; HIP if the read fails. */
+ * strip waits that ran out of time (DIST_GEMM_OPT_WAIT_LIMIT_US) in all
+ * single-launch runs of the plan so far; each such workgroup copied its
+ * strip itself, so results stay correct.  0 on an unshared device.
+ * INVALID_ARG for NULL arguments; HIP if the read fails. */
 int dist_gemm_device_errors(dist_gemm_plan_t plan, int64_t* count);
 
 /* Synchronise the plan's streams, free its staging, streams and events, and

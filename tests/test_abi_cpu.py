@@ -44,7 +44,7 @@ def test_step_table_matches_oracle(sched, S):
     for g, r in zip(got, ref):
         step, shard, staged, slot, m0, m1, n0, n1 = g
         assert (step, shard, staged, m0, m1, n0, n1) == (r.s, r.shard, r.staged, r.m0, r.m1, r.n0, r.n1)
-        assert slot == (step - 1 if staged else -1)
+        assert slot == (shard if staged else -1)
 
 
 def test_p2_local_shape_from_step_table():
@@ -76,6 +76,7 @@ def test_null_handles_are_rejected_without_gpu():
     assert dg.lib.dist_gemm_set_bias(None, None) == -1
     assert dg.lib.dist_gemm_set_option(None, 0, 1) == -1
     assert dg.lib.dist_gemm_run(None, None, None, None, None, 1.0, 0.0, None) == -1
+    assert dg.lib.dist_gemm_run_ag(None, None, None, None, None, None, 1.0, 0.0, None) == -1
     assert dg.lib.dist_gemm_destroy(None) == 0
     n = ctypes.c_int(0)
     assert dg.lib.dist_gemm_step_table(8, 8, 16, 1, 2, 0, 0, None, None) == -1
@@ -84,7 +85,7 @@ def test_null_handles_are_rejected_without_gpu():
     assert dg.lib.dist_gemm_step_timeline(None, None, ctypes.byref(n)) == -1
     c = ctypes.c_int64(0)
     assert dg.lib.dist_gemm_device_errors(None, ctypes.byref(c)) == -1
-    for opt in range(11):
+    for opt in range(12):
         assert dg.lib.dist_gemm_set_option(None, opt, 1) == -1
 
 

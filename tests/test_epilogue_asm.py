@@ -1,11 +1,15 @@
 """The fp32 epilogue with C streams C into LDS with buffer_load ... lds and
 waits for each 16-row part with s_waitcnt vmcnt immediates derived from its
 own issue order (C loads and D stores share the counter and retire in order).
-Those immediates are only right if the compiler puts no other vector-memory
-instruction (a register spill, a reload) between a C load and its wait.  This
-test compiles the GEMM units to gfx950 assembly with the library's flags and
-checks, in every kernel that has the epilogue, that its vector-memory
-instructions from the first C load on are exactly the designed sequence.
+A wait vmcnt(N) covers a C load once at least N vector-memory operations
+were issued after it, so the immediates are right as long as the compiler
+issues exactly the designed loads and stores, in that order: a missing or
+moved one would let a wait pass early.  An extra one (a register spill or
+reload) only makes a wait stricter.  This test compiles the GEMM units to
+gfx950 assembly with the library's flags and checks, in every kernel that
+has the epilogue, that its global and buffer memory instructions contain
+the designed sequence with nothing else in between (scratch spills and
+reloads, if any, are reported and allowed).
 
 CPU only (hipcc cross-compiles); skipped where hipcc is missing.
 """
@@ -61,29 +65,28 @@ def _expected():
 
 
 def _vm_sequence(body):
-    """Vector-memory instructions after the last MFMA, from the first LDS DMA
-    on: 'C' for a C load into LDS, 'S' for a 16-byte global store, else the
-    mnemonic; cut once all the epilogue's stores have been seen."""
+    """Vector-memory instructions after the last MFMA: 'C' for a load into
+    LDS, 'S' for a 16-byte global store, else the mnemonic.  (The persistent
+    kernels also place their shard-copy loop there, which loads into LDS too.)"""
     last_mfma = max(i for i, l in enumerate(body) if "v_mfma" in l)
-    seq, started = [], False
-    want_stores = PARTS * PER_PART
+    seq = []
     for line in body[last_mfma:]:
         tok = line.split()
         if not tok or tok[0].startswith((";", ".")):
             continue
         op = tok[0]
         if "offen lds" in line:
-            started = True
             seq.append("C")
-        elif not started:
-            continue
         elif op == "global_store_dwordx4":
             seq.append("S")
         elif op.startswith(("global_", "buffer_", "flat_", "scratch_")):
             seq.append(op)
-        if seq.count("S") == want_stores:
-            break
     return seq
+
+
+def _contains(seq, pattern):
+    n = len(pattern)
+    return any(seq[i:i + n] == pattern for i in range(len(seq) - n + 1))
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
@@ -103,7 +106,12 @@ def test_c_epilogue_memory_sequence(tmp_path):
             if not any("offen lds" in l for l in body[last_mfma:]):
                 continue  # no C epilogue in this kernel (bf16 output)
             seq = _vm_sequence(body)
-            assert seq == expected, (name, seq[:80])
+            spills = [op for op in seq if op.startswith("scratch_")]
+            seq = [op for op in seq if not op.startswith("scratch_")]
+            # the designed sequence, with no other global or buffer access in between
+            assert _contains(seq, expected), (name, seq[:160])
+            if spills:
+                print(f"{name}: {len(spills)} scratch accesses after the last MFMA (allowed)")
             checked.append(name)
     # fp32 output: bf16 / fp32 / e4m3 inputs, per-step and persistent kernels
     assert len(checked) == 6, checked

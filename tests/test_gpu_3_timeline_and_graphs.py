@@ -53,8 +53,11 @@ def test_step_timeline(sched, group):
 
 
 def test_single_launch_timeline():
-    """A single-launch run is one launch: every step reports its span, and no
-    separate copy completion (the copies are inside the launch)."""
+    """A single-launch run reports the device's own stamps per step: the last
+    strip of a staged step complete, and the first and last tile of the step.
+    Here (1024 columns over 8 steps) every 256-column strip straddles two
+    shards and belongs to the later one, so the even steps have no strip and
+    report -1; the odd steps report copies, then tiles, inside the launch."""
     import torch
     import communication_tensor_gemm_amd as dg
     w = workloads.small_case("tl_single", "AG_ROT_B", "BF16_F32", 1024, 1024, 256, 1, 8, 1.0, 0.0,
@@ -71,8 +74,15 @@ def test_single_launch_timeline():
         tl = p.step_timeline()
         times = p.step_times()
     check_full(w, x, D)
-    assert len({(b, e) for _, b, e in tl}) == 1
-    assert all(c == -1.0 and 0.0 <= b <= e for c, b, e in tl)
+    log("timeline", tl)
+    assert [s for s, (_, b, _) in enumerate(tl) if b >= 0] == [1, 3, 5, 7]
+    for s, (c, b, e) in enumerate(tl):
+        if s % 2 == 0:
+            assert (c, b, e) == (-1.0, -1.0, -1.0)
+        else:
+            # a strip's tiles start only once it is complete; the step's last
+            # strip may complete after its first tile began (tile-granular)
+            assert 0.0 <= c <= e and 0.0 <= b <= e
     assert len(times) == 2 * w.TP and all(t > 0 for t in times)
 
 
