@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     dist_gemm_plan_steps,
     dist_gemm_run,
     dist_gemm_run_ag,
+    dist_gemm_run_noalloc,
     dist_gemm_set_bias,
     dist_gemm_set_option,
     dist_gemm_set_scales,

@@ -27,8 +27,8 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM",
 
 # C functions declared in include/distgemm.h (checked by the CPU tests)
 C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
-               "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_plan_steps",
-               "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
+               "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_run_noalloc",
+               "dist_gemm_plan_steps", "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                "dist_gemm_destroy", "dist_gemm_last_error", "dist_gemm_status_string")
 
 
@@ -68,6 +68,9 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_set_option.argtypes = [vp, i32, i64]
     lib.dist_gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     lib.dist_gemm_run_ag.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+    f32 = ctypes.c_float
+    lib.dist_gemm_run_noalloc.argtypes = [i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, f32, f32, f32,
+                                          f32, vp]
     lib.dist_gemm_plan_steps.argtypes = [vp, ctypes.POINTER(Step), ctypes.POINTER(i32)]
     lib.dist_gemm_step_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.dist_gemm_step_timeline.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
@@ -78,7 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_status_string.argtypes = [i32]
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
     for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
-                 "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_plan_steps",
+                 "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_run_noalloc",
+                 "dist_gemm_plan_steps",
                  "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                  "dist_gemm_destroy"):
         getattr(lib, name).restype = i32
@@ -152,6 +156,13 @@ def dist_gemm_run(plan, A, B, C, D, alpha: float = 1.0, beta: float = 0.0, strea
 def dist_gemm_run_ag(plan, A, B, C, D, ag_out, alpha: float = 1.0, beta: float = 0.0, stream=None):
     _check(lib.dist_gemm_run_ag(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(ag_out), alpha, beta,
                                 _stream(stream)), plan)
+
+
+def dist_gemm_run_noalloc(M, N, K, L, TP, schedule, dtype, A, B, C, D, alpha: float = 1.0,
+                          beta: float = 0.0, scale_a: float = 1.0, scale_b: float = 1.0, stream=None):
+    _check(lib.dist_gemm_run_noalloc(M, N, K, L, TP, _enum(SCHEDULES, schedule), _enum(DTYPES, dtype),
+                                     _ptr(A), _ptr(B), _ptr(C), _ptr(D), alpha, beta, scale_a, scale_b,
+                                     _stream(stream)))
 
 
 def dist_gemm_plan_steps(plan) -> List[tuple]:

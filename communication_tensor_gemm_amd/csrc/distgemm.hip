@@ -547,18 +547,34 @@ int alloc_fused(dist_gemm_plan_s* P, std::string* err) {
 // then groups of max_group consecutive steps), which segment carries (or
 // claims) each step's copy, the piece size of each step, and each queue's
 // item ranges.  Synchronous (plan creation and option changes only).
-int build_fused(dist_gemm_plan_s* P, std::string* err) {
-  const Problem& pr = P->pr;
+// Host tables of one single-launch configuration.
+struct FusedTables {
+  std::vector<dg::FusedSeg> segs;
+  std::vector<dg::FusedStepCopy> copies;
+  std::vector<int32_t> strips;  // strip list, then the step of each position
+  std::vector<int32_t> seg;     // [nq][n_segs + 1]
+  uint64_t align = 0;           // OR of the contiguous piece sizes
+};
+
+struct FusedOpts {
+  int queues = dg::kMaxQueues;
+  int64_t copy_chunk = 2 << 20;
+  int copy_ahead = 4;
+  int max_group = 2;
+};
+
+int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, const FusedOpts& o,
+                  FusedTables* out, std::string* err) {
   const int S = pr.S;
-  const int nq = P->queues;
+  const int nq = o.queues;
   const StripGeom sg = strip_geom(pr);
-  const int ns = P->n_strips;
+  const int ns = static_cast<int>((sg.ext + dg::kBM - 1) / dg::kBM);
   const int64_t w = sg.ext / S;  // shard width along the strip dimension
   const int64_t L = pr.L;
   const int64_t other = sg.cols ? (pr.M + dg::kBM - 1) / dg::kBM : (pr.N + dg::kBN - 1) / dg::kBN;
 
   std::vector<int> step_of_shard(S, 0);
-  for (const dist_gemm_step& st : P->steps) step_of_shard[st.shard] = st.step;
+  for (const dist_gemm_step& st : steps) step_of_shard[st.shard] = st.step;
   std::vector<int> sstep(ns, 0);
   for (int k = 0; k < ns; ++k) {
     const int64_t r0 = static_cast<int64_t>(k) * dg::kBM;
@@ -580,7 +596,7 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
   // segments
   std::vector<std::pair<int, int>> segr;  // first and last step
   segr.push_back({0, 0});
-  for (int h = 1; h < S; h += P->max_group) segr.push_back({h, std::min(S - 1, h + P->max_group - 1)});
+  for (int h = 1; h < S; h += o.max_group) segr.push_back({h, std::min(S - 1, h + o.max_group - 1)});
   const int G = static_cast<int>(segr.size());
   std::vector<int> seg_of(S, 0);
   std::vector<dg::FusedSeg> segs(G);
@@ -613,7 +629,7 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
       carrier = 0;  // step 0's tiles never wait: they may carry their own strips
     } else {
       const int sh = seg_of[h];
-      for (int g = sh - P->copy_ahead; g >= 0 && carrier < 0; --g)
+      for (int g = sh - o.copy_ahead; g >= 0 && carrier < 0; --g)
         if (segs[g].tiles > 0) carrier = g;
       for (int g = 0; g < sh && carrier < 0; ++g)
         if (segs[g].tiles > 0) carrier = g;
@@ -641,7 +657,7 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
       if (n2 == 0 || h2 == 0) continue;
       int c2 = -1;
       const int sh2 = seg_of[h2];
-      for (int g = sh2 - P->copy_ahead; g >= 0 && c2 < 0; --g)
+      for (int g = sh2 - o.copy_ahead; g >= 0 && c2 < 0; --g)
         if (segs[g].tiles > 0) c2 = g;
       for (int g = 0; g < sh2 && c2 < 0; ++g)
         if (segs[g].tiles > 0) c2 = g;
@@ -653,7 +669,7 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
     int64_t piece = (total + 4 * ctiles - 1) / (4 * ctiles);
     piece = std::max<int64_t>(4096, (piece + 15) / 16 * 16);
     if (piece > 32768) piece = (piece + 32767) / 32768 * 32768;
-    piece = std::min<int64_t>(P->copy_chunk, piece);
+    piece = std::min<int64_t>(o.copy_chunk, piece);
     int64_t per;
     if (!sg.strided) {
       c.piece = piece;
@@ -670,7 +686,6 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
   }
   // (the carrier segment does not decrease with the step, so every segment
   // carries a contiguous range of steps, and claims only steps of its own)
-  P->n_segs = G;
   // queue q: its share of every segment's tiles (a contiguous range of the
   // segment's tile order per batch), segment after segment
   std::vector<int32_t> seg(static_cast<size_t>(nq) * (G + 1), 0);
@@ -684,15 +699,38 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
     }
     seg[static_cast<size_t>(q) * (G + 1) + G] = static_cast<int32_t>(at);
   }
-  std::vector<int32_t> strips(list);
-  strips.insert(strips.end(), lstep.begin(), lstep.end());
-  DG_HIP(err, hipMemcpy(P->d_segs, segs.data(), sizeof(dg::FusedSeg) * G, hipMemcpyHostToDevice));
-  DG_HIP(err, hipMemcpy(P->d_copies, cps.data(), sizeof(dg::FusedStepCopy) * S, hipMemcpyHostToDevice));
-  DG_HIP(err, hipMemcpy(P->d_strips, strips.data(), sizeof(int32_t) * strips.size(), hipMemcpyHostToDevice));
-  DG_HIP(err, hipMemcpy(P->d_seg, seg.data(), seg.size() * sizeof(int32_t), hipMemcpyHostToDevice));
-  P->fused_align = 0;
-  for (const dg::FusedStepCopy& c : cps)
-    if (!sg.strided) P->fused_align |= static_cast<uint64_t>(c.piece);
+  out->strips = list;
+  out->strips.insert(out->strips.end(), lstep.begin(), lstep.end());
+  out->segs = std::move(segs);
+  out->copies = std::move(cps);
+  out->seg = std::move(seg);
+  out->align = 0;
+  for (const dg::FusedStepCopy& c : out->copies)
+    if (!sg.strided) out->align |= static_cast<uint64_t>(c.piece);
+  return DIST_GEMM_OK;
+}
+
+FusedOpts plan_opts(const dist_gemm_plan_s* P) {
+  FusedOpts o;
+  o.queues = P->queues;
+  o.copy_chunk = P->copy_chunk;
+  o.copy_ahead = P->copy_ahead;
+  o.max_group = P->max_group;
+  return o;
+}
+
+// Compute the plan's tables and copy them to its device tables.
+int build_fused(dist_gemm_plan_s* P, std::string* err) {
+  FusedTables t;
+  const int rc = compute_fused(P->pr, P->steps, plan_opts(P), &t, err);
+  if (rc != DIST_GEMM_OK) return rc;
+  DG_HIP(err, hipMemcpy(P->d_segs, t.segs.data(), sizeof(dg::FusedSeg) * t.segs.size(), hipMemcpyHostToDevice));
+  DG_HIP(err, hipMemcpy(P->d_copies, t.copies.data(), sizeof(dg::FusedStepCopy) * t.copies.size(),
+                        hipMemcpyHostToDevice));
+  DG_HIP(err, hipMemcpy(P->d_strips, t.strips.data(), sizeof(int32_t) * t.strips.size(), hipMemcpyHostToDevice));
+  DG_HIP(err, hipMemcpy(P->d_seg, t.seg.data(), t.seg.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  P->n_segs = static_cast<int>(t.segs.size());
+  P->fused_align = t.align;
   return DIST_GEMM_OK;
 }
 
@@ -708,15 +746,28 @@ FusedOrder& fused_order() {
   return *o;
 }
 
-int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B, const void* C,
-              void* D, uint8_t* G, float alpha, float beta, const void* copy_src, bool copy_on,
-              bool copy_local, uint64_t* times, uint64_t* times_next) {
-  const Problem& pr = P->pr;
+// Device tables and counters of a single-launch run.
+struct FusedDevice {
+  const dg::FusedSeg* segs;
+  const dg::FusedStepCopy* copies;
+  const int32_t* strips;  // list, then steps
+  const int32_t* seg;
+  uint32_t* ctr;
+  int32_t* sync;
+  int n_strips, n_segs;
+  uint64_t piece_align;
+};
+
+// Arguments of one single-launch run of the problem pr.
+dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, const void* A, const void* B,
+                         const void* C, void* D, const void* bias, uint8_t* G, float alpha, float beta,
+                         const void* copy_src, bool copy_on, bool copy_local, int64_t spin_ticks,
+                         int64_t delay_ticks) {
   const StripGeom sg = strip_geom(pr);
   dg::FusedArgs a{};
   dg::GemmParams& g = a.g;
   g.A = A; g.B = B; g.C = beta != 0.0f ? C : nullptr; g.D = D;
-  g.bias = P->bias;
+  g.bias = bias;
   g.lda = pr.K; g.ldb = pr.K; g.ldc = pr.N; g.ldd = pr.N;
   g.sA = pr.shared_a ? 0 : pr.M * pr.K; g.sB = pr.N * pr.K; g.sC = pr.M * pr.N; g.sD = pr.M * pr.N;
   g.M = static_cast<int32_t>(pr.M); g.N = static_cast<int32_t>(pr.N);
@@ -724,59 +775,81 @@ int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B,
   g.alpha = alpha; g.beta = beta;
   a.gath = G;
   a.src = static_cast<const uint8_t*>(copy_src);
-  a.segs = P->d_segs;
-  a.steps = P->d_copies;
-  a.strip_list = P->d_strips;
-  a.strip_step = P->d_strips + P->n_strips;
-  a.seg = P->d_seg;
-  a.sync = P->d_sync;
-  a.ctr = P->d_ctr;
-  a.times = times;
-  a.times_next = times_next;
+  a.segs = dv.segs;
+  a.steps = dv.copies;
+  a.strip_list = dv.strips;
+  a.strip_step = dv.strips + dv.n_strips;
+  a.seg = dv.seg;
+  a.sync = dv.sync;
+  a.ctr = dv.ctr;
   a.row_bytes = sg.row_bytes;
   a.ext = sg.ext;
   a.gbatch = sg.gbatch;
   a.pitch = sg.pitch;
   a.height = sg.height;
-  a.spin_limit = P->wait_limit_us * P->clock_khz / 1000;
-  a.delay = P->copy_delay_us * P->clock_khz / 1000;
+  a.spin_limit = spin_ticks;
+  a.delay = delay_ticks;
   a.rot = sg.rot;
   a.cols = sg.cols;
   a.strided = sg.strided;
-  a.n_strips = P->n_strips;
+  a.n_strips = dv.n_strips;
   a.LG = sg.LG;
   uint64_t align = reinterpret_cast<uint64_t>(copy_src) | reinterpret_cast<uint64_t>(G) |
-                   static_cast<uint64_t>(sg.row_bytes) | static_cast<uint64_t>(sg.gbatch) | P->fused_align;
+                   static_cast<uint64_t>(sg.row_bytes) | static_cast<uint64_t>(sg.gbatch) | dv.piece_align;
   if (sg.strided)
     align |= static_cast<uint64_t>(sg.pitch) | static_cast<uint64_t>(dg::kBN * sg.row_bytes) |
              static_cast<uint64_t>(sg.ext * sg.row_bytes);
   a.unit = (align % 16 == 0) ? 16 : (align % 4 == 0) ? 4 : 1;
-  a.n_seg = P->n_segs;
-  a.nq = P->queues;
+  a.n_seg = dv.n_segs;
+  a.nq = queues;
   a.S = pr.S;
   a.copy_on = copy_on ? 1 : 0;
   a.copy_local = copy_local ? 1 : 0;
-  const int grid = std::max(P->queues, P->n_cu / P->queues * P->queues);
+  return a;
+}
 
+// Enqueue a single-launch run on st, ordered after the device's previous one
+// unless st is capturing; `before` (if any) is enqueued between the wait and
+// the launch.
+template <typename Before>
+int launch_ordered(int device, int in_kind, int out_kind, const dg::FusedArgs& a, int grid, hipStream_t st,
+                   std::string* err, Before before) {
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  DG_HIP(&P->err, hipStreamIsCapturing(st, &cap));
+  DG_HIP(err, hipStreamIsCapturing(st, &cap));
   const bool ordered = cap == hipStreamCaptureStatusNone;
   FusedOrder& o = fused_order();
   std::unique_lock<std::mutex> lock(o.mu);
   if (ordered) {
-    if (static_cast<int>(o.tail.size()) <= P->device) {
-      o.tail.resize(P->device + 1, nullptr);
-      o.live.resize(P->device + 1, 0);
+    if (static_cast<int>(o.tail.size()) <= device) {
+      o.tail.resize(device + 1, nullptr);
+      o.live.resize(device + 1, 0);
     }
-    if (!o.tail[P->device]) DG_HIP(&P->err, hipEventCreateWithFlags(&o.tail[P->device], hipEventDisableTiming));
-    if (o.live[P->device]) DG_HIP(&P->err, hipStreamWaitEvent(st, o.tail[P->device], 0));
+    if (!o.tail[device]) DG_HIP(err, hipEventCreateWithFlags(&o.tail[device], hipEventDisableTiming));
+    if (o.live[device]) DG_HIP(err, hipStreamWaitEvent(st, o.tail[device], 0));
   }
-  DG_HIP(&P->err, dg::launch_fused(pr.in_kind, pr.out_kind, a, grid, st));
+  const int rc = before();
+  if (rc != DIST_GEMM_OK) return rc;
+  DG_HIP(err, dg::launch_fused(in_kind, out_kind, a, grid, st));
   if (ordered) {
-    DG_HIP(&P->err, hipEventRecord(o.tail[P->device], st));
-    o.live[P->device] = 1;
+    DG_HIP(err, hipEventRecord(o.tail[device], st));
+    o.live[device] = 1;
   }
   return DIST_GEMM_OK;
+}
+
+int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B, const void* C,
+              void* D, uint8_t* G, float alpha, float beta, const void* copy_src, bool copy_on,
+              bool copy_local, uint64_t* times, uint64_t* times_next) {
+  const Problem& pr = P->pr;
+  FusedDevice dv{P->d_segs, P->d_copies, P->d_strips, P->d_seg, P->d_ctr, P->d_sync,
+                 P->n_strips, P->n_segs, P->fused_align};
+  dg::FusedArgs a = fused_args(pr, dv, P->queues, A, B, C, D, P->bias, G, alpha, beta, copy_src, copy_on,
+                               copy_local, P->wait_limit_us * P->clock_khz / 1000,
+                               P->copy_delay_us * P->clock_khz / 1000);
+  a.times = times;
+  a.times_next = times_next;
+  const int grid = std::max(P->queues, P->n_cu / P->queues * P->queues);
+  return launch_ordered(P->device, pr.in_kind, pr.out_kind, a, grid, st, &P->err, [] { return DIST_GEMM_OK; });
 }
 
 // Change a plan setting that the single-launch tables depend on: wait for
@@ -799,6 +872,103 @@ int change_tables(dist_gemm_plan_t plan, Apply apply, Undo undo) {
     (void)build_fused(plan, nullptr);
   }
   return rc;
+}
+
+// ---- Allocation-free runs -------------------------------------------------
+//
+// dist_gemm_run_noalloc keeps what a plan allocates -- the gathered image,
+// the single-launch tables and the counters -- in one file-scope device
+// array, `scratch`, of fixed size: every GPU that runs it holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (in host code that name is a host-side stand-in, not a device
+// address): each device's address comes from hipGetSymbolAddress on that
+// device at its first call.  A small kernel writes each call's tables
+// (passed by value) and zeroes the counters, so nothing is copied from host
+// memory at run time and a call can be captured into a graph.
+
+constexpr size_t kNoAllocGatherBytes = size_t{32} << 20;  // largest gathered image
+constexpr size_t kNoAllocTableBytes = size_t{256} << 10;  // tables and counters
+constexpr int kNoAllocMaxSteps = 16;
+constexpr int kNoAllocMaxStrips = 128;
+// table region: segments, step copies, strips, queue items, sync words, counters
+constexpr size_t kNaSegs = 0, kNaCopies = 1024, kNaStrips = 2048, kNaSeg = 4096, kNaSync = 8192,
+                 kNaCtr = 16384;
+static_assert(sizeof(dg::FusedSeg) * kNoAllocMaxSteps <= kNaCopies - kNaSegs, "no-alloc layout");
+static_assert(sizeof(dg::FusedStepCopy) * kNoAllocMaxSteps <= kNaStrips - kNaCopies, "no-alloc layout");
+static_assert(sizeof(int32_t) * 2 * kNoAllocMaxStrips <= kNaSeg - kNaStrips, "no-alloc layout");
+static_assert(sizeof(int32_t) * dg::kMaxQueues * (kNoAllocMaxSteps + 1) <= kNaSync - kNaSeg, "no-alloc layout");
+static_assert(sizeof(int32_t) * (dg::kSyncClaim + kNoAllocMaxSteps) * dg::kSyncStride <= kNaCtr - kNaSync,
+              "no-alloc layout");
+
+struct NoAllocPack {
+  dg::FusedSeg segs[kNoAllocMaxSteps];
+  dg::FusedStepCopy copies[kNoAllocMaxSteps];
+  int32_t strips[2 * kNoAllocMaxStrips];
+  int32_t seg[dg::kMaxQueues * (kNoAllocMaxSteps + 1)];
+  int32_t n_segs, n_strips, S, n_ctr;
+};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocGatherBytes + kNoAllocTableBytes];
+
+namespace {
+
+// Write one call's tables into the table region and zero its counters.
+__global__ __launch_bounds__(256) void noalloc_setup_kernel(NoAllocPack pk, uint8_t* tables) {
+  const int t = threadIdx.x;
+  for (int i = t; i < pk.n_segs; i += 256)
+    reinterpret_cast<dg::FusedSeg*>(tables + kNaSegs)[i] = pk.segs[i];
+  for (int i = t; i < pk.S; i += 256)
+    reinterpret_cast<dg::FusedStepCopy*>(tables + kNaCopies)[i] = pk.copies[i];
+  for (int i = t; i < 2 * pk.n_strips; i += 256) reinterpret_cast<int32_t*>(tables + kNaStrips)[i] = pk.strips[i];
+  for (int i = t; i < dg::kMaxQueues * (pk.n_segs + 1); i += 256)
+    reinterpret_cast<int32_t*>(tables + kNaSeg)[i] = pk.seg[i];
+  for (int i = t; i < dg::sync_words(pk.S); i += 256) reinterpret_cast<int32_t*>(tables + kNaSync)[i] = 0;
+  for (int i = t; i < pk.n_ctr; i += 256) reinterpret_cast<uint32_t*>(tables + kNaCtr)[i] = 0;
+}
+
+// Per device: the address of `scratch`, and the device properties a run needs.
+struct NoAllocDevice {
+  uint8_t* ptr = nullptr;
+  int n_cu = 256;
+  int64_t clock_khz = 100000;
+};
+std::mutex g_noalloc_mu;
+std::vector<NoAllocDevice> g_noalloc_dev;
+
+int noalloc_device(int dev, NoAllocDevice* out) {
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (static_cast<int>(g_noalloc_dev.size()) <= dev) g_noalloc_dev.resize(dev + 1);
+  NoAllocDevice& d = g_noalloc_dev[dev];
+  if (!d.ptr) {
+    hipDeviceProp_t prop;
+    DG_HIP(nullptr, hipGetDeviceProperties(&prop, dev));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(nullptr, DIST_GEMM_ERR_UNSUPPORTED,
+                  std::string("this library is built for gfx950 only; device is ") + prop.gcnArchName);
+    void* p = nullptr;
+    DG_HIP(nullptr, hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(nullptr, DIST_GEMM_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    d.n_cu = std::max(1, prop.multiProcessorCount);
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+      d.clock_khz = khz;
+    {
+      // the event that orders single-launch runs on the device, made now so
+      // that no later call creates anything
+      FusedOrder& o = fused_order();
+      std::lock_guard<std::mutex> olock(o.mu);
+      if (static_cast<int>(o.tail.size()) <= dev) {
+        o.tail.resize(dev + 1, nullptr);
+        o.live.resize(dev + 1, 0);
+      }
+      if (!o.tail[dev]) DG_HIP(nullptr, hipEventCreateWithFlags(&o.tail[dev], hipEventDisableTiming));
+    }
+    d.ptr = static_cast<uint8_t*>(p);
+  }
+  *out = d;
+  return DIST_GEMM_OK;
 }
 
 }  // namespace
@@ -1298,6 +1468,85 @@ int dist_gemm_destroy(dist_gemm_plan_t plan) {
   DeviceGuard guard(plan->device);
   release(plan);
   return DIST_GEMM_OK;
+}
+
+int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+                          const void* A, const void* B, const void* C, void* D, float alpha, float beta,
+                          float scale_a, float scale_b, void* stream) {
+  Problem pr;
+  int rc = validate(M, N, K, L, TP, schedule, dtype, &pr, nullptr);
+  if (rc != DIST_GEMM_OK) return rc;
+  if (!A || !B || !D) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "A, B and D must be non-NULL");
+  if (beta != 0.0f && !C) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "C is NULL but beta != 0");
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !std::isfinite(scale_a) || !std::isfinite(scale_b))
+    return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "alpha, beta and the scales must be finite");
+  if (D == A || D == B) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "D must not alias A or B");
+  const std::vector<dist_gemm_step> steps = build_steps(pr);
+  const bool rotating = pr.schedule != DIST_GEMM_MONOLITHIC && pr.S > 1;
+  const CopyGeom cg = copy_geom(pr);
+  const StripGeom sgeo = strip_geom(pr);
+  const int n_strips = rotating ? static_cast<int>((sgeo.ext + dg::kBM - 1) / dg::kBM) : 0;
+  const int64_t n_ctr = rotating ? static_cast<int64_t>(pr.L) * (n_strips + pr.S) : 0;
+  if (rotating && (pr.S > kNoAllocMaxSteps || n_strips > kNoAllocMaxStrips || cg.alloc > kNoAllocGatherBytes ||
+                   kNaCtr + static_cast<size_t>(n_ctr) * sizeof(uint32_t) > kNoAllocTableBytes))
+    return fail(nullptr, DIST_GEMM_ERR_UNSUPPORTED,
+                "dist_gemm_run_noalloc handles at most " + std::to_string(kNoAllocMaxSteps) + " steps, " +
+                    std::to_string(kNoAllocMaxStrips) + " strips of 256 along the rotated dimension, a " +
+                    std::to_string(kNoAllocGatherBytes >> 20) + " MiB gathered operand and " +
+                    std::to_string((kNoAllocTableBytes - kNaCtr) / 4) + " strip counters; this problem needs " +
+                    std::to_string(pr.S) + " steps, " + std::to_string(n_strips) + " strips, " +
+                    std::to_string(cg.alloc) + " bytes and " + std::to_string(n_ctr) + " counters");
+  int dev = 0;
+  DG_HIP(nullptr, hipGetDevice(&dev));
+  NoAllocDevice nd;
+  rc = noalloc_device(dev, &nd);
+  if (rc != DIST_GEMM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float alpha_eff = (pr.in_kind == dg::IN_E4M3) ? alpha * scale_a * scale_b : alpha;
+  if (!rotating) {
+    // one GEMM over the whole problem: no scratch
+    dg::GemmParams g{};
+    g.A = A; g.B = B; g.C = beta != 0.0f ? C : nullptr; g.D = D; g.bias = nullptr;
+    g.lda = pr.K; g.ldb = pr.K; g.ldc = pr.N; g.ldd = pr.N;
+    g.sA = pr.M * pr.K; g.sB = pr.N * pr.K; g.sC = pr.M * pr.N; g.sD = pr.M * pr.N;
+    g.M = static_cast<int32_t>(pr.M); g.N = static_cast<int32_t>(pr.N);
+    g.K = static_cast<int32_t>(pr.K); g.L = static_cast<int32_t>(pr.L);
+    g.alpha = alpha_eff; g.beta = beta;
+    DG_HIP(nullptr, dg::launch_gemm(pr.in_kind, pr.out_kind, g, st));
+    return DIST_GEMM_OK;
+  }
+  FusedTables t;
+  rc = compute_fused(pr, steps, FusedOpts{}, &t, nullptr);
+  if (rc != DIST_GEMM_OK) return rc;
+  NoAllocPack pk{};
+  for (size_t i = 0; i < t.segs.size(); ++i) pk.segs[i] = t.segs[i];
+  for (size_t i = 0; i < t.copies.size(); ++i) pk.copies[i] = t.copies[i];
+  for (size_t i = 0; i < t.strips.size(); ++i) pk.strips[i] = t.strips[i];
+  for (size_t i = 0; i < t.seg.size(); ++i) pk.seg[i] = t.seg[i];
+  pk.n_segs = static_cast<int32_t>(t.segs.size());
+  pk.n_strips = n_strips;
+  pk.S = pr.S;
+  pk.n_ctr = static_cast<int32_t>(n_ctr);
+  uint8_t* const tables = nd.ptr + kNoAllocGatherBytes;
+  FusedDevice dv{reinterpret_cast<const dg::FusedSeg*>(tables + kNaSegs),
+                 reinterpret_cast<const dg::FusedStepCopy*>(tables + kNaCopies),
+                 reinterpret_cast<const int32_t*>(tables + kNaStrips), reinterpret_cast<const int32_t*>(tables + kNaSeg),
+                 reinterpret_cast<uint32_t*>(tables + kNaCtr), reinterpret_cast<int32_t*>(tables + kNaSync),
+                 n_strips, pk.n_segs, t.align};
+  const bool copy_on = !(reduce_scatter(pr.schedule) && beta == 0.0f);
+  const void* copy_src = pr.schedule == DIST_GEMM_AG_ROT_A ? A : pr.schedule == DIST_GEMM_AG_ROT_B ? B : C;
+  const int64_t spin = int64_t{1000000} * nd.clock_khz / 1000;  // 1 s, as the plans' default
+  const dg::FusedArgs a = fused_args(pr, dv, dg::kMaxQueues, A, B, C, D, nullptr, nd.ptr, alpha_eff, beta,
+                                     copy_src, copy_on, false, spin, 0);
+  const int grid = std::max(dg::kMaxQueues, nd.n_cu / dg::kMaxQueues * dg::kMaxQueues);
+  std::string err;
+  rc = launch_ordered(dev, pr.in_kind, pr.out_kind, a, grid, st, &err, [&]() -> int {
+    hipLaunchKernelGGL(noalloc_setup_kernel, dim3(1), dim3(256), 0, st, pk, tables);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DIST_GEMM_OK : hip_fail(&err, e, "no-alloc table setup");
+  });
+  if (rc != DIST_GEMM_OK) g_last_error = err;
+  return rc;
 }
 
 }  // extern "C"

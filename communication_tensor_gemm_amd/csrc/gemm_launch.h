@@ -81,14 +81,14 @@ constexpr int kMaxQueues = 8;
 constexpr int kSyncExit = kMaxQueues;
 constexpr int kSyncErr = kMaxQueues + 1;
 constexpr int kSyncClaim = kMaxQueues + 2;
-inline int sync_words(int S) { return (kSyncClaim + S) * kSyncStride; }
+__host__ __device__ inline int sync_words(int S) { return (kSyncClaim + S) * kSyncStride; }
 
 // Device timeline of one run (unsigned 64-bit wall-clock ticks), written
 // with atomic max only: [0] = ~(first workgroup start); per step s,
 // [1 + 3s] = last piece of the step's copy counted, [2 + 3s] = ~(first
 // tile of the step begins), [3 + 3s] = last tile of the step ends.  Zero
 // at the start of the run (the previous launch zeroes it at its end).
-inline int timeline_words(int S) { return 1 + 3 * S; }
+__host__ __device__ inline int timeline_words(int S) { return 1 + 3 * S; }
 
 struct FusedArgs {
   GemmParams g;                  // the whole problem on the monolithic tile grid

@@ -311,6 +311,33 @@ int dist_gemm_run(dist_gemm_plan_t plan, const void* A, const void* B, const voi
 int dist_gemm_run_ag(dist_gemm_plan_t plan, const void* A, const void* B, const void* C, void* D,
                      void* ag_out, float alpha, float beta, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: one run
+ * of the problem (M, N, K, L, TP, schedule, dtype; same validation and
+ * layouts as dist_gemm_plan and dist_gemm_run) with no plan, computing
+ *   D = alpha*scale_a*scale_b*(A B) + beta*C
+ * exactly as a plan's default single-launch run does (bit for bit), with
+ * scale_a / scale_b as dist_gemm_set_scales (ignored unless the dtype is an
+ * E4M3 one; pass 1.0f).  It allocates nothing: the gathered image, the
+ * single-launch tables and the counters live in one file-scope device array
+ * of 32 MiB + 256 KiB that every GPU running this call holds until the
+ * process ends (its address taken on each device's first call, which also
+ * creates the event that orders single-launch runs on the device).  Limits
+ * (UNSUPPORTED, with a message, beyond them): at most 16 steps, at most 128
+ * strips of 256 rows (AG_ROT_A, RS_TILE_A_ROT_C) or columns (AG_ROT_B,
+ * RS_TILE_B_ROT_C), a gathered rotating operand of at most 32 MiB
+ * (L x M x K, L x N x K or L x M x N elements), and L x (strips + steps) at
+ * most 61440.  MONOLITHIC or TP = 1 runs one GEMM and uses no scratch.
+ * Calls on one GPU share the array, which keeps the last call's contents
+ * (each call rewrites its tables and clears its counters first): calls that
+ * overlap on one GPU race, so issue them on one stream, or order them; the
+ * library orders uncaptured calls on a device after one another anyway.
+ * Errors: as dist_gemm_plan plus dist_gemm_run; the message is read with
+ * dist_gemm_last_error(NULL). */
+int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+                          const void* A, const void* B, const void* C, void* D, float alpha, float beta,
+                          float scale_a, float scale_b, void* stream);
+
 /* Query the plan's step table (same contents as dist_gemm_step_table). */
 int dist_gemm_plan_steps(dist_gemm_plan_t plan, dist_gemm_step* out, int* n_steps);
 
