@@ -125,4 +125,7 @@ def round_to(x: np.ndarray, elem: str) -> np.ndarray:
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     if elem == "bf16":
         return f64_to_bf16_value(x)
+    if elem == "e4m3":
+        # the fp8 output cast saturates at +-448 (the largest finite e4m3fn)
+        return e4m3_to_f64(f64_to_e4m3(x, saturate=True))
     raise ValueError(elem)

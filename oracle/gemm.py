@@ -1,4 +1,4 @@
-"""The step-scheduled fp64 GEMM  D = alpha * (sa*A) * (sb*B) + beta * C (+ bias).
+"""The step-scheduled fp64 GEMM  D = s * (alpha * (sa*A) * (sb*B) + beta * C (+ bias)).
 
 Definition followed: the CUTLASS Distributed GEMM pages compare the
 distributed result against a single-device GEMM with the epilogue scalars
@@ -6,8 +6,11 @@ alpha (default 1) and beta (default 0) (example page, "Getting started"); the
 PyTorch symmetric-memory page defines the fused all-gather matmul as
 all_gather then matmul, the fused matmul reduce-scatter as matmul then
 reduce_scatter, and the scaled variants as _scaled_mm with per-tensor
-scale_a / scale_b and an optional bias added to every row of the product
-(the op schemas and their fallbacks).
+scale_a / scale_b, an optional bias added to every row of the product, and
+a result scale s for an fp8 output (the op schemas and their fallbacks; the
+pages pass scale_result through to _scaled_mm without defining it, read
+here as a factor on the whole result before its one rounding to the output
+element, s = 1 for the other outputs).
 
 The oracle walks the same step table as the GPU path: one numpy float64
 matmul per step on that step's row or column block, the epilogue in fp64,
@@ -48,7 +51,7 @@ def _bias(bias, out_elem: str):
 
 def dist_gemm(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem: str,
               out_elem: str, scale_a: float = 1.0, scale_b: float = 1.0,
-              rank: int = 0, bias=None) -> np.ndarray:
+              rank: int = 0, bias=None, result_scale: float = 1.0) -> np.ndarray:
     """Unrounded fp64 D* of the whole schedule, shape L x M x N."""
     Ah, Bh, Ch = decode_operands(_as3(A), _as3(B), _as3(C), in_elem, out_elem, scale_a, scale_b)
     bh = _bias(bias, out_elem)
@@ -67,14 +70,14 @@ def dist_gemm(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem
                 blk = blk + np.float64(beta) * Ch[l, st.m0:st.m1, st.n0:st.n1]
             if bh is not None:                              # bias: one value per column
                 blk = blk + bh[st.n0:st.n1][None, :]
-            D[l, st.m0:st.m1, st.n0:st.n1] = blk
+            D[l, st.m0:st.m1, st.n0:st.n1] = np.float64(result_scale) * blk
     return D
 
 
 def dist_gemm_sampled(A, B, C, alpha: float, beta: float, schedule: str, S: int, in_elem: str,
                       out_elem: str, rows: Sequence[int], cols: Sequence[int],
                       scale_a: float = 1.0, scale_b: float = 1.0, batch: int = 0,
-                      rank: int = 0, bias=None):
+                      rank: int = 0, bias=None, result_scale: float = 1.0):
     """D* on the sub-grid rows x cols of batch `batch`, visiting the same steps.
 
     Only the sampled rows of A and columns of B are decoded, so this runs at
@@ -103,7 +106,7 @@ def dist_gemm_sampled(A, B, C, alpha: float, beta: float, schedule: str, S: int,
             blk = blk + np.float64(beta) * c[np.ix_(ri, ci)]
         if bh is not None:
             blk = blk + bh[ci][None, :]
-        D[np.ix_(ri, ci)] = blk
+        D[np.ix_(ri, ci)] = np.float64(result_scale) * blk
     return D, np.linalg.norm(a, axis=1), np.linalg.norm(b, axis=1)
 
 
@@ -112,7 +115,8 @@ def round_output(D: np.ndarray, out_elem: str) -> np.ndarray:
 
 
 def gemm_unchunked(A, B, C, alpha: float, beta: float, in_elem: str, out_elem: str,
-                   scale_a: float = 1.0, scale_b: float = 1.0, bias=None) -> np.ndarray:
+                   scale_a: float = 1.0, scale_b: float = 1.0, bias=None,
+                   result_scale: float = 1.0) -> np.ndarray:
     """The same definition evaluated as one fp64 matmul per batch, no steps."""
     Ah, Bh, Ch = decode_operands(_as3(A), _as3(B), _as3(C), in_elem, out_elem, scale_a, scale_b)
     D = np.float64(alpha) * np.matmul(Ah, np.transpose(Bh, (0, 2, 1)))
@@ -120,7 +124,7 @@ def gemm_unchunked(A, B, C, alpha: float, beta: float, in_elem: str, out_elem: s
         D = D + np.float64(beta) * Ch
     if bias is not None:
         D = D + _bias(bias, out_elem)[None, None, :]
-    return D
+    return np.float64(result_scale) * D
 
 
 def step_flops(schedule: str, M: int, N: int, K: int, S: int, L: int = 1):

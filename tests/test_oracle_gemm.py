@@ -321,3 +321,50 @@ def test_reduce_scatter_chain_with_bias(sched, op):
     # and not the other reduction: avg and sum differ by a factor TP
     other = want * TP if op == "avg" else want / TP
     assert not np.allclose(part[0], other)
+
+
+def _torch_e4m3_nearest(x):
+    """Nearest e4m3fn value to each float64 x (ties to the even code), from
+    torch's decoding of all 256 codes, clipped to +-448 (the saturating
+    cast): a rounding written independently of the oracle's encoder."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).double().numpy()
+    fin = np.isfinite(vals)
+    v, c = vals[fin], np.arange(256)[fin]
+    out = np.empty_like(np.asarray(x, dtype=np.float64))
+    for i, xi in enumerate(np.clip(np.asarray(x, dtype=np.float64).ravel(), -448.0, 448.0)):
+        d = np.abs(v - xi)
+        best = np.nonzero(d == d.min())[0]
+        if len(best) > 1:   # a tie: the even code (mantissa bit 0 clear)
+            best = [b for b in best if c[b] % 2 == 0]
+        out.flat[i] = v[best[0]]
+    return out
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_brute_force_result_scale_e4m3_output(sched):
+    """The scaled matmul with an fp8 output: D = round_e4m3(s * (alpha*sa*sb*A B
+    + beta*C)), s the result scale; exact rational arithmetic for the sum,
+    rounding checked against torch's decoded e4m3 values."""
+    S = 2 if sched != "MONOLITHIC" else 1
+    for M, N, K, s in ((4, 6, 32, 0.3), (8, 4, 16, -2.75), (2, 8, 64, 7.0)):
+        w, x = _inputs("E4M3_E4M3", M, N, K, beta=0.5, seed=M * 10 + N)
+        ex, mag = _brute(x.A, x.B, x.C, 1.25, 0.5, "e4m3", "e4m3", x.scale_a, x.scale_b)
+        D = gemm.dist_gemm(x.A, x.B, x.C, 1.25, 0.5, sched, S, "e4m3", "e4m3", x.scale_a, x.scale_b,
+                           result_scale=s)
+        want = np.vectorize(float)(ex) * s
+        assert np.all(np.abs(D - want) <= 4 * K * 2.0 ** -53 * abs(s) * mag + 1e-300)
+        got = gemm.round_output(D, "e4m3")
+        assert np.array_equal(got, _torch_e4m3_nearest(D))
+        assert np.all(np.abs(got) <= 448.0)
+
+
+def test_result_scale_saturates_the_fp8_cast():
+    w, x = _inputs("E4M3_E4M3", 8, 8, 32, beta=0.0, seed=5)
+    D1 = gemm.dist_gemm(x.A, x.B, None, 1.0, 0.0, "AG_ROT_A", 2, "e4m3", "e4m3", x.scale_a, x.scale_b)
+    big = 2000.0 / np.abs(D1).max()
+    D = gemm.dist_gemm(x.A, x.B, None, 1.0, 0.0, "AG_ROT_A", 2, "e4m3", "e4m3", x.scale_a, x.scale_b,
+                       result_scale=big)
+    r = gemm.round_output(D, "e4m3")
+    assert np.abs(D).max() > 448.0
+    assert np.all(r[np.abs(D) >= 448.0] == np.sign(D[np.abs(D) >= 448.0]) * 448.0)

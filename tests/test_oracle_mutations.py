@@ -40,8 +40,19 @@ MUTATIONS = [
     ("oracle/parity.py", "den = den + np.abs(np.asarray(bias, dtype=np.float64))[None, :]",
      "den = den + np.abs(np.asarray(bias, dtype=np.float64))[:, None]"),
     ("oracle/parity.py", "den = abs(alpha) * np.outer(row_norms, col_norms)", "den = alpha * np.outer(row_norms, col_norms)"),
-    ("oracle/parity.py", "tight = bool(np.all(diff <= 2.0 ** -8 * np.abs(D_star) + t * den))",
-     "tight = bool(np.all(diff <= 2.0 ** -7 * np.abs(D_star) + t * den))"),
+    ("oracle/parity.py", "tight = bool(np.all(diff <= 2.0 ** -8 * np.abs(ref) + t * den))",
+     "tight = bool(np.all(diff <= 2.0 ** -7 * np.abs(ref) + t * den))"),
+    # the result scale of an fp8 output, and the e4m3 output cast
+    ("oracle/gemm.py", "D[l, st.m0:st.m1, st.n0:st.n1] = np.float64(result_scale) * blk",
+     "D[l, st.m0:st.m1, st.n0:st.n1] = blk"),
+    ("oracle/parity.py", "return abs(result_scale) * den", "return den"),
+    ("oracle/parity.py", "return abs(result_scale) * den", "return result_scale * den"),
+    ("oracle/parity.py", "return np.clip(D_star, -codecs.E4M3_MAX, codecs.E4M3_MAX)", "return D_star"),
+    ("oracle/parity.py", "tight = bool(np.all(diff <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -10 + t * den))",
+     "tight = bool(np.all(diff <= 2.0 ** -3 * np.abs(ref) + 2.0 ** -10 + t * den))"),
+    ("oracle/parity.py", "tight = bool(np.all(diff <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -10 + t * den))",
+     "tight = bool(np.all(diff <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 + t * den))"),
+    ("oracle/codecs.py", "return e4m3_to_f64(f64_to_e4m3(x, saturate=True))", "return e4m3_to_f64(f64_to_e4m3(x, saturate=False))"),
 ]
 
 

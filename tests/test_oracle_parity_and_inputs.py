@@ -178,3 +178,39 @@ def test_bf16_output_tight_bar_is_half_an_ulp_of_rounding():
     dev = Dstar.copy()
     dev[7, 9] = Dstar[7, 9] * (1 + 1.5 * 2.0 ** -8)
     assert not parity.check(dev, Dstar, rn, rn, 1.0, 0.0, None, "bf16", "bf16")[2]
+
+
+@pytest.mark.parametrize("s", [2.5, -4.0])
+def test_metric_result_scale_scales_the_bar(s):
+    """The result scale multiplies the whole result, so its magnitude scales
+    the normaliser; planted errors on both sides of the bar."""
+    rn = np.random.default_rng(6).uniform(1.0, 3.0, 6)
+    cn = np.random.default_rng(7).uniform(1.0, 3.0, 5)
+    g = np.random.default_rng(8)
+    Dstar = g.standard_normal((6, 5))
+    for factor, want in ((0.3, True), (3.0, False)):
+        dev = Dstar.copy()
+        den = abs(s) * 2.0 * rn[2] * cn[3]
+        dev[2, 3] += factor * parity.BARS["f32"] * den
+        assert parity.check(dev, Dstar, rn, cn, 2.0, 0.0, None, "f32", "f32", None, s)[0] == want
+
+
+def test_e4m3_output_bars():
+    """e4m3 output: the cast saturates at 448 (a saturated result is exact);
+    the tight bar is half a spacing of three mantissa bits (2^-4 relative,
+    2^-10 absolute below 2^-6), no more."""
+    rn = np.full(4, 1e-3)
+    # 100 -> 104: half a spacing (8); 6.5 * 2^-9 -> 6 * 2^-9: half the subnormal spacing
+    Dstar = np.array([[500.0, -1000.0, 100.0, 6.5 * 2.0 ** -9]] * 4)
+    dev = np.array([[448.0, -448.0, 104.0, 6.0 * 2.0 ** -9]] * 4)
+    ok, mx, tight, _ = parity.check(dev, Dstar, rn, rn, 1.0, 0.0, None, "e4m3", "e4m3")
+    assert tight
+    bad = dev.copy()
+    bad[1, 0] = 416.0           # one spacing below the saturated value
+    assert not parity.check(bad, Dstar, rn, rn, 1.0, 0.0, None, "e4m3", "e4m3")[2]
+    bad = dev.copy()
+    bad[2, 2] = 112.0           # a full spacing off 100
+    assert not parity.check(bad, Dstar, rn, rn, 1.0, 0.0, None, "e4m3", "e4m3")[2]
+    bad = dev.copy()
+    bad[3, 3] = 7.7 * 2.0 ** -9  # subnormal region: 1.2 * 2^-9 off, beyond half the spacing
+    assert not parity.check(bad, Dstar, rn, rn, 1.0, 0.0, None, "e4m3", "e4m3")[2]

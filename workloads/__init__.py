@@ -31,6 +31,7 @@ DTYPES = {
     "BF16_BF16": ("bf16", "bf16"),
     "E4M3_BF16": ("e4m3", "bf16"),
     "E4M3_F32": ("e4m3", "f32"),
+    "E4M3_E4M3": ("e4m3", "e4m3"),
 }
 E4M3_MAX = 448.0
 
