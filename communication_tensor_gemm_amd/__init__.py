@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     dist_gemm_run_noalloc,
     dist_gemm_set_bias,
     dist_gemm_set_option,
+    dist_gemm_set_result_scale,
     dist_gemm_set_scales,
     dist_gemm_step_table,
     dist_gemm_step_times,

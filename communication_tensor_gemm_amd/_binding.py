@@ -16,17 +16,18 @@ LIB_PATH = os.path.join(_HERE, "libdistgemm.so")
 
 SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_C": 3,
              "MONOLITHIC": 4}
-DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4}
+DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4, "E4M3_E4M3": 5}
 OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2, "COPY_STREAMS": 3,
            "STEP_GROUP": 4, "EXECUTION": 5, "QUEUES": 6, "COPY_CHUNK": 7, "WAIT_LIMIT_US": 8,
-           "COPY_AHEAD": 9, "SHARED_A": 10, "COPY_DELAY_US": 11}
+           "COPY_AHEAD": 9, "SHARED_A": 10, "COPY_DELAY_US": 11, "FAST_ACCUM": 12}
 # bytes per element of (A/B, C/D) for each dtype
 ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
-              "E4M3_F32": (1, 4)}
+              "E4M3_F32": (1, 4), "E4M3_E4M3": (1, 1)}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM", -5: "HIP"}
 
 # C functions declared in include/distgemm.h (checked by the CPU tests)
-C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
+C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_result_scale",
+               "dist_gemm_set_bias",
                "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_run_noalloc",
                "dist_gemm_plan_steps", "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
                "dist_gemm_destroy", "dist_gemm_last_error", "dist_gemm_status_string")
@@ -65,6 +66,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_plan.argtypes = [i64, i64, i64, i64, i32, i32, i32, ctypes.POINTER(vp)]
     lib.dist_gemm_set_scales.argtypes = [vp, ctypes.c_float, ctypes.c_float]
     lib.dist_gemm_set_bias.argtypes = [vp, vp]
+    lib.dist_gemm_set_result_scale.argtypes = [vp, ctypes.c_float]
     lib.dist_gemm_set_option.argtypes = [vp, i32, i64]
     lib.dist_gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     lib.dist_gemm_run_ag.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
@@ -80,7 +82,8 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_last_error.restype = ctypes.c_char_p
     lib.dist_gemm_status_string.argtypes = [i32]
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
-    for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_bias",
+    for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_result_scale",
+                 "dist_gemm_set_bias",
                  "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_run_noalloc",
                  "dist_gemm_plan_steps",
                  "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
@@ -121,6 +124,10 @@ def dist_gemm_plan(M, N, K, L, TP, schedule, dtype) -> ctypes.c_void_p:
 
 def dist_gemm_set_scales(plan, scale_a: float, scale_b: float):
     _check(lib.dist_gemm_set_scales(plan, scale_a, scale_b), plan)
+
+
+def dist_gemm_set_result_scale(plan, scale_result: float):
+    _check(lib.dist_gemm_set_result_scale(plan, scale_result), plan)
 
 
 def dist_gemm_set_bias(plan, bias):
@@ -213,6 +220,9 @@ class Plan:
 
     def set_scales(self, scale_a, scale_b):
         dist_gemm_set_scales(self.handle, scale_a, scale_b)
+
+    def set_result_scale(self, scale_result):
+        dist_gemm_set_result_scale(self.handle, scale_result)
 
     def set_bias(self, bias):
         """bias: a GPU tensor of N output elements (fp32, or bf16 bits), or None.

@@ -60,6 +60,7 @@ int dtype_kinds(int dtype, int* in_kind, int* out_kind) {
     case DIST_GEMM_BF16_BF16: *in_kind = dg::IN_BF16; *out_kind = dg::OUT_BF16; return 0;
     case DIST_GEMM_E4M3_BF16: *in_kind = dg::IN_E4M3; *out_kind = dg::OUT_BF16; return 0;
     case DIST_GEMM_E4M3_F32: *in_kind = dg::IN_E4M3; *out_kind = dg::OUT_F32; return 0;
+    case DIST_GEMM_E4M3_E4M3: *in_kind = dg::IN_E4M3; *out_kind = dg::OUT_E4M3; return 0;
     default: return -1;
   }
 }
@@ -227,6 +228,8 @@ struct dist_gemm_plan_s {
   bool captured = false;      // a run was captured into a graph: tables are fixed
   std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
+  float result_scale = 1.0f;   // e4m3 output only
+  int fast_accum = 0;          // accepted; gfx950 MFMAs accumulate in fp32 either way
   const void* bias = nullptr;  // device, N values of the output type, or NULL
   int compute_streams = 2;
   int copy_engine = 2;  // library streaming copy kernel
@@ -449,6 +452,7 @@ dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, 
   g.L = static_cast<int32_t>(P->pr.L);
   g.alpha = alpha;
   g.beta = beta;
+  g.post = P->result_scale;
   g.M = y.M;
   g.N = y.N;
   g.A = (y.stagedA ? stg : static_cast<const uint8_t*>(A)) + y.offA;
@@ -761,7 +765,7 @@ struct FusedDevice {
 // Arguments of one single-launch run of the problem pr.
 dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, const void* A, const void* B,
                          const void* C, void* D, const void* bias, uint8_t* G, float alpha, float beta,
-                         const void* copy_src, bool copy_on, bool copy_local, int64_t spin_ticks,
+                         float post, const void* copy_src, bool copy_on, bool copy_local, int64_t spin_ticks,
                          int64_t delay_ticks) {
   const StripGeom sg = strip_geom(pr);
   dg::FusedArgs a{};
@@ -772,7 +776,7 @@ dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, c
   g.sA = pr.shared_a ? 0 : pr.M * pr.K; g.sB = pr.N * pr.K; g.sC = pr.M * pr.N; g.sD = pr.M * pr.N;
   g.M = static_cast<int32_t>(pr.M); g.N = static_cast<int32_t>(pr.N);
   g.K = static_cast<int32_t>(pr.K); g.L = static_cast<int32_t>(pr.L);
-  g.alpha = alpha; g.beta = beta;
+  g.alpha = alpha; g.beta = beta; g.post = post;
   a.gath = G;
   a.src = static_cast<const uint8_t*>(copy_src);
   a.segs = dv.segs;
@@ -843,8 +847,8 @@ int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B,
   const Problem& pr = P->pr;
   FusedDevice dv{P->d_segs, P->d_copies, P->d_strips, P->d_seg, P->d_ctr, P->d_sync,
                  P->n_strips, P->n_segs, P->fused_align};
-  dg::FusedArgs a = fused_args(pr, dv, P->queues, A, B, C, D, P->bias, G, alpha, beta, copy_src, copy_on,
-                               copy_local, P->wait_limit_us * P->clock_khz / 1000,
+  dg::FusedArgs a = fused_args(pr, dv, P->queues, A, B, C, D, P->bias, G, alpha, beta, P->result_scale,
+                               copy_src, copy_on, copy_local, P->wait_limit_us * P->clock_khz / 1000,
                                P->copy_delay_us * P->clock_khz / 1000);
   a.times = times;
   a.times_next = times_next;
@@ -1080,6 +1084,17 @@ int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b) {
   return DIST_GEMM_OK;
 }
 
+int dist_gemm_set_result_scale(dist_gemm_plan_t plan, float scale_result) {
+  if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
+  if (!std::isfinite(scale_result))
+    return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "the result scale must be finite");
+  if (plan->pr.out_kind != dg::OUT_E4M3 && scale_result != 1.0f)
+    return fail(&plan->err, DIST_GEMM_ERR_UNSUPPORTED,
+                "a result scale applies to an fp8 (E4M3) output; this plan's output is not fp8");
+  plan->result_scale = scale_result;
+  return DIST_GEMM_OK;
+}
+
 int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias) {
   if (!plan) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "plan is NULL");
   plan->bias = bias;
@@ -1160,6 +1175,11 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       if (value < 0 || value > 100000000)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "wait limit must be in [0, 1e8] us");
       plan->wait_limit_us = value;
+      return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_FAST_ACCUM:
+      if (value != 0 && value != 1)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "fast accumulate must be 0 or 1");
+      plan->fast_accum = static_cast<int>(value);
       return DIST_GEMM_OK;
     case DIST_GEMM_OPT_COPY_DELAY_US:
       if (value < 0 || value > 1000000)
@@ -1511,7 +1531,7 @@ int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, in
     g.sA = pr.M * pr.K; g.sB = pr.N * pr.K; g.sC = pr.M * pr.N; g.sD = pr.M * pr.N;
     g.M = static_cast<int32_t>(pr.M); g.N = static_cast<int32_t>(pr.N);
     g.K = static_cast<int32_t>(pr.K); g.L = static_cast<int32_t>(pr.L);
-    g.alpha = alpha_eff; g.beta = beta;
+    g.alpha = alpha_eff; g.beta = beta; g.post = 1.0f;
     DG_HIP(nullptr, dg::launch_gemm(pr.in_kind, pr.out_kind, g, st));
     return DIST_GEMM_OK;
   }
@@ -1537,7 +1557,7 @@ int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, in
   const void* copy_src = pr.schedule == DIST_GEMM_AG_ROT_A ? A : pr.schedule == DIST_GEMM_AG_ROT_B ? B : C;
   const int64_t spin = int64_t{1000000} * nd.clock_khz / 1000;  // 1 s, as the plans' default
   const dg::FusedArgs a = fused_args(pr, dv, dg::kMaxQueues, A, B, C, D, nullptr, nd.ptr, alpha_eff, beta,
-                                     copy_src, copy_on, false, spin, 0);
+                                     1.0f, copy_src, copy_on, false, spin, 0);
   const int grid = std::max(dg::kMaxQueues, nd.n_cu / dg::kMaxQueues * dg::kMaxQueues);
   std::string err;
   rc = launch_ordered(dev, pr.in_kind, pr.out_kind, a, grid, st, &err, [&]() -> int {

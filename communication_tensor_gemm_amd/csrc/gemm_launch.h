@@ -7,10 +7,11 @@ namespace dg {
 
 // Element type of A/B, and of C/D.
 enum InKind { IN_F32 = 0, IN_BF16 = 1, IN_E4M3 = 2 };
-enum OutKind { OUT_F32 = 0, OUT_BF16 = 1 };
+enum OutKind { OUT_F32 = 0, OUT_BF16 = 1, OUT_E4M3 = 2 };
 
 // One GEMM over an (M x N) block of D, full K:
 //   D[i][j] = alpha * sum_k A[i][k] * B[j][k] + beta * C[i][j] (+ bias[j])
+// (with an e4m3 output, the sum times `post` before the cast)
 // A rows are lda apart, B rows (the N index) ldb apart, both K-contiguous.
 // Strides and leading dimensions are in elements of the operand's type.
 struct GemmParams {
@@ -23,6 +24,7 @@ struct GemmParams {
   int64_t sA, sB, sC, sD;  // batch strides
   int32_t M, N, K, L;
   float alpha, beta;
+  float post;  // e4m3 output: the result scale, applied before the cast
 };
 
 // Macro tile of one workgroup, and the bytes of one operand row per K tile.
@@ -31,7 +33,7 @@ constexpr int kBN = 256;
 constexpr int kRowBytes = 128;
 
 inline int in_elem_size(int in_kind) { return in_kind == IN_F32 ? 4 : (in_kind == IN_BF16 ? 2 : 1); }
-inline int out_elem_size(int out_kind) { return out_kind == OUT_F32 ? 4 : 2; }
+inline int out_elem_size(int out_kind) { return out_kind == OUT_F32 ? 4 : (out_kind == OUT_BF16 ? 2 : 1); }
 
 // ---- Single-launch run: device-side strip readiness -----------------------
 //

@@ -15,6 +15,7 @@ hipError_t launch_gemm(int in_kind, int out_kind, const GemmParams& p, hipStream
   if (p.M <= 0 || p.N <= 0 || p.L <= 0) return hipSuccess;
   if (in_kind == IN_E4M3 && out_kind == OUT_BF16) return launch_t<IN_E4M3, OUT_BF16>(p, stream);
   if (in_kind == IN_E4M3 && out_kind == OUT_F32) return launch_t<IN_E4M3, OUT_F32>(p, stream);
+  if (in_kind == IN_E4M3 && out_kind == OUT_E4M3) return launch_t<IN_E4M3, OUT_E4M3>(p, stream);
   return launch_gemm_mfma16(in_kind, out_kind, p, stream);
 }
 
@@ -23,6 +24,7 @@ hipError_t launch_fused(int in_kind, int out_kind, const FusedArgs& a, int grid,
   if (grid <= 0) return hipSuccess;
   if (in_kind == IN_E4M3 && out_kind == OUT_BF16) return launch_fused_t<IN_E4M3, OUT_BF16>(a, grid, stream);
   if (in_kind == IN_E4M3 && out_kind == OUT_F32) return launch_fused_t<IN_E4M3, OUT_F32>(a, grid, stream);
+  if (in_kind == IN_E4M3 && out_kind == OUT_E4M3) return launch_fused_t<IN_E4M3, OUT_E4M3>(a, grid, stream);
   return launch_fused_mfma16(in_kind, out_kind, a, grid, stream);
 }
 

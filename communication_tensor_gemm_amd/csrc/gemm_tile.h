@@ -142,13 +142,47 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// OCP e4m3fn (sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+// infinities; S.1111.111 is NaN; largest finite 448; subnormals m * 2^-9),
+// from the format's definition.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 24, e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 15u && m == 7u) return __builtin_bit_cast(float, sign | 0x7fc00000u);
+  if (e == 0u) return __builtin_bit_cast(float, sign | __builtin_bit_cast(uint32_t, static_cast<float>(m) * 0.001953125f));
+  return __builtin_bit_cast(float, sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// fp32 -> e4m3fn, round to nearest even, saturating at +-448 (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // |f| >= 448 (infinities too)
+  if (a < 0x3c800000u) {
+    // below 2^-6: multiples of 2^-9; 8 * 2^-9 is the smallest normal (code 8)
+    const float q = __builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+    return sign | static_cast<uint32_t>(q);
+  }
+  // normal: keep three mantissa bits, ties to even; the carry may raise the exponent
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  const uint32_t code = r - ((127u - 7u) << 3);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+template <int OUT>
+constexpr int out_size() {
+  return OUT == OUT_F32 ? 4 : (OUT == OUT_BF16 ? 2 : 1);
+}
+
 template <int OUT>
 __device__ __forceinline__ float load_out(const void* C, int64_t idx) {
   if constexpr (OUT == OUT_F32) {
     return static_cast<const float*>(C)[idx];
-  } else {
+  } else if constexpr (OUT == OUT_BF16) {
     const uint32_t h = static_cast<const uint16_t*>(C)[idx];
     return __builtin_bit_cast(float, h << 16);
+  } else {
+    return e4m3_to_f32(static_cast<const uint8_t*>(C)[idx]);
   }
 }
 
@@ -156,8 +190,10 @@ template <int OUT>
 __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
   if constexpr (OUT == OUT_F32) {
     static_cast<float*>(D)[idx] = v;
-  } else {
+  } else if constexpr (OUT == OUT_BF16) {
     static_cast<uint16_t*>(D)[idx] = f32_to_bf16_rne(v);
+  } else {
+    static_cast<uint8_t*>(D)[idx] = static_cast<uint8_t>(f32_to_e4m3_rne_sat(v));
   }
 }
 
@@ -369,7 +405,7 @@ template <typename M, int OUT>
 __device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc (&acc)[M::NB][M::NB],
                                                 const GemmParams& p, uint8_t* Dw, const uint8_t* Cw,
                                                 const uint8_t* Bw, int rows_left, int cols_left) {
-  constexpr int OES = OUT == OUT_F32 ? 4 : 2;
+  constexpr int OES = out_size<OUT>();
   // the lane's bias values, one per column block (Bw: the wave's first column)
   float bv[M::NB];
 #pragma unroll
@@ -392,6 +428,7 @@ __device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc 
           float v = p.alpha * acc[i][j][r];
           if (crow) v = __builtin_fmaf(p.beta, load_out<OUT>(crow, col), v);
           if (Bw) v += bv[j];
+          if constexpr (OUT == OUT_E4M3) v *= p.post;
           store_out<OUT>(drow, col, v);
         }
       }
@@ -815,7 +852,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   // (and C, bias) rows 16-byte aligned, each 32-row quarter of the wave's block goes through
   // LDS so that every lane stores 16 contiguous bytes; otherwise element by
   // element.
-  constexpr int OES = OUT == OUT_F32 ? 4 : 2;
+  constexpr int OES = out_size<OUT>();
   const bool use_c = p.beta != 0.0f;
   const uint8_t* Dl = static_cast<const uint8_t*>(p.D) + l * p.sD * OES;
   const uint8_t* Cl = use_c ? static_cast<const uint8_t*>(p.C) + l * p.sC * OES : nullptr;
@@ -833,7 +870,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   int elane = lane;
   asm volatile("" : "+v"(elane));
   // the condition is uniform over the workgroup (the barrier inside needs that)
-  if constexpr (OUT == OUT_F32) {
+  if constexpr (OUT == OUT_E4M3) {
+    // e4m3 output: element by element (one byte per value)
+  } else if constexpr (OUT == OUT_F32) {
     if ((align & 15) == 0) {
       epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
       return;

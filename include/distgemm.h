@@ -93,14 +93,19 @@ enum dist_gemm_schedule {
  *   BF16_BF16 : A,B bf16;            C,D bf16 (round to nearest even)
  *   E4M3_BF16 : A,B OCP e4m3fn;      C,D bf16; per-tensor scales apply
  *   E4M3_F32  : A,B OCP e4m3fn;      C,D fp32; per-tensor scales apply
- * The scaled fp8 form follows _scaled_mm's scale_a / scale_b on the PyTorch
- * symmetric-memory page (fused_all_gather_scaled_matmul). */
+ *   E4M3_E4M3 : A,B OCP e4m3fn;      C,D OCP e4m3fn (round to nearest even,
+ *               saturating at +-448; NaN stays NaN); per-tensor scales and
+ *               the result scale apply
+ * The scaled fp8 form follows _scaled_mm's scale_a / scale_b / scale_result
+ * / out_dtype on the PyTorch symmetric-memory page
+ * (fused_all_gather_scaled_matmul, fused_scaled_matmul_reduce_scatter). */
 enum dist_gemm_dtype {
   DIST_GEMM_F32 = 0,
   DIST_GEMM_BF16_F32 = 1,
   DIST_GEMM_BF16_BF16 = 2,
   DIST_GEMM_E4M3_BF16 = 3,
-  DIST_GEMM_E4M3_F32 = 4
+  DIST_GEMM_E4M3_F32 = 4,
+  DIST_GEMM_E4M3_E4M3 = 5
 };
 
 /* One row of the step table (host data). */
@@ -139,11 +144,21 @@ int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int sched
  * Returns INVALID_ARG for a NULL plan or non-finite scales. */
 int dist_gemm_set_scales(dist_gemm_plan_t plan, float scale_a, float scale_b);
 
+/* Result scale of the scaled matmul with an fp8 output (the `scale_result`
+ * argument that the fused scaled ops of the PyTorch symmetric-memory page
+ * pass to _scaled_mm): runs after this call compute, for dtype E4M3_E4M3,
+ *   D = cast_e4m3(scale_result * (alpha*scale_a*scale_b*(A B) + beta*C + bias))
+ * the product, C and bias summed in fp32, then multiplied, then cast once.
+ * Default 1.0.  INVALID_ARG for a NULL plan or a non-finite scale;
+ * UNSUPPORTED for a scale other than 1.0 on a plan whose output is not
+ * E4M3 (the result scale exists for fp8 outputs). */
+int dist_gemm_set_result_scale(dist_gemm_plan_t plan, float scale_result);
+
 /* Bias of the scaled matmul (the `bias` argument of _scaled_mm in the op
  * schemas of the PyTorch symmetric-memory page): runs after this call compute
  *   D = alpha*scale_a*scale_b*(A B) + beta*C + bias[j]
  * for every row i and batch of column j.  `bias` is a device pointer to N
- * values of the output element type (fp32 or bf16), read by every later run
+ * values of the output element type (fp32, bf16 or e4m3), read by every later run
  * of the plan, so it must stay allocated while those runs may execute; the
  * plan does not own it.  NULL (the default) removes the bias.  16-byte
  * alignment (fp32 output) or 8-byte alignment (bf16 output) keeps the
@@ -233,6 +248,12 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     With AG_ROT_A the A shards are rotated once for all L products.
  *     0 (default) = A has L batches like the other operands.  Waits for the
  *     plan's last run when it changes.
+ *   DIST_GEMM_OPT_FAST_ACCUM: 0 (default) or 1, the use_fast_accum flag of
+ *     the fused scaled ops on the PyTorch symmetric-memory page.  It trades
+ *     accumulation precision for speed on parts whose fp8 matrix units
+ *     accumulate in reduced precision unless asked not to; gfx950's
+ *     f8f6f4 MFMA accumulates in fp32 at full rate, so both settings run the
+ *     same kernel and give the same bits.
  *   DIST_GEMM_OPT_COPY_DELAY_US: a test hook that holds back every shard
  *     copy by this many microseconds, in [0, 10^6] (default 0): in mode 1
  *     each workgroup starts its first copy piece no earlier than this long
@@ -255,7 +276,8 @@ enum dist_gemm_option {
   DIST_GEMM_OPT_WAIT_LIMIT_US = 8,
   DIST_GEMM_OPT_COPY_AHEAD = 9,
   DIST_GEMM_OPT_SHARED_A = 10,
-  DIST_GEMM_OPT_COPY_DELAY_US = 11
+  DIST_GEMM_OPT_COPY_DELAY_US = 11,
+  DIST_GEMM_OPT_FAST_ACCUM = 12
 };
 int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
 

@@ -31,6 +31,9 @@ def empty_out(w: workloads.Workload, fill=np.nan):
     shape = (w.L, w.M, w.N)
     if w.out_dtype == "f32":
         return torch.full(shape, float(fill), dtype=torch.float32, device="cuda")
+    if w.out_dtype == "e4m3":
+        # e4m3fn stored as uint8 bit patterns; 0x7F is NaN
+        return torch.full(shape, 0x7F, dtype=torch.uint8, device="cuda")
     # bf16 stored as int16 bit patterns; 0x7FC0 is a NaN pattern
     return torch.full(shape, 0x7FC0, dtype=torch.int16, device="cuda")
 
@@ -39,11 +42,13 @@ def from_gpu_out(t, out_elem):
     a = t.cpu().numpy()
     if out_elem == "f32":
         return a.astype(np.float64)
+    if out_elem == "e4m3":
+        return codecs.e4m3_to_f64(a.view(np.uint8))
     return codecs.bf16_to_f64(a.view(np.uint16))
 
 
 def run_plan(w: workloads.Workload, x: workloads.Inputs, schedule=None, TP=None, dev=None,
-             out=None, options=None, alpha=None, beta=None):
+             out=None, options=None, alpha=None, beta=None, result_scale=None):
     """Run one dist_gemm_run and synchronize.  Returns the output tensor."""
     import torch
     import communication_tensor_gemm_amd as dg
@@ -58,6 +63,8 @@ def run_plan(w: workloads.Workload, x: workloads.Inputs, schedule=None, TP=None,
     with dg.Plan(w.M, w.N, w.K, w.L, TP, schedule, w.dtype) as plan:
         if w.in_dtype == "e4m3":
             plan.set_scales(x.scale_a, x.scale_b)
+        if result_scale is not None:
+            plan.set_result_scale(result_scale)
         for k, v in (options or {}).items():
             plan.set_option(k, v)
         plan.run(A, B, C if beta != 0.0 else None, D, alpha, beta)
@@ -65,7 +72,7 @@ def run_plan(w: workloads.Workload, x: workloads.Inputs, schedule=None, TP=None,
     return D
 
 
-def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None, bias=None):
+def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None, bias=None, result_scale=1.0):
     """Element-by-element comparison with the full oracle.  Returns max err.
     bias: the bias bytes (N output elements) the run used, or None."""
     schedule = schedule or w.schedule
@@ -74,7 +81,7 @@ def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None, bias=None
     beta = w.beta if beta is None else beta
     Dstar = gemm.dist_gemm(x.A, x.B, x.C if beta != 0 else None, alpha, beta, schedule,
                            TP if schedule != "MONOLITHIC" else 1, w.in_dtype, w.out_dtype,
-                           x.scale_a, x.scale_b, bias=bias)
+                           x.scale_a, x.scale_b, bias=bias, result_scale=result_scale)
     bdec = None if bias is None else codecs.decode(np.asarray(bias).reshape(-1), w.out_dtype)
     got = from_gpu_out(D, w.out_dtype)
     worst = 0.0
@@ -84,7 +91,7 @@ def check_full(w, x, D, schedule=None, TP=None, alpha=None, beta=None, bias=None
         c = None if beta == 0 else codecs.decode(x.C[l], w.out_dtype)
         ok, mx, tight, _ = parity.check(got[l], Dstar[l], np.linalg.norm(a, axis=1),
                                         np.linalg.norm(b, axis=1), alpha, beta, c,
-                                        w.in_dtype, w.out_dtype, bdec)
+                                        w.in_dtype, w.out_dtype, bdec, result_scale)
         assert ok, f"{w.name} batch {l}: max normalised error {mx}"
         assert tight, f"{w.name} batch {l}: tight bar failed (max err {mx})"
         worst = max(worst, mx)

@@ -85,7 +85,8 @@ def test_null_handles_are_rejected_without_gpu():
     assert dg.lib.dist_gemm_step_timeline(None, None, ctypes.byref(n)) == -1
     c = ctypes.c_int64(0)
     assert dg.lib.dist_gemm_device_errors(None, ctypes.byref(c)) == -1
-    for opt in range(12):
+    assert dg.lib.dist_gemm_set_result_scale(None, 1.0) == -1
+    for opt in range(13):
         assert dg.lib.dist_gemm_set_option(None, opt, 1) == -1
 
 
