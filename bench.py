@@ -458,7 +458,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # untimed runs before each timed set: the clock dips for the first tens of
+    # runs of a sudden sustained load and recovers after about a hundred
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--compute-streams", type=int, default=2)
     ap.add_argument("--copy-engine", type=int, default=2,
@@ -469,7 +471,8 @@ def main():
                     help="0 = step launches + side-stream copies, 1 = one persistent launch per run")
     ap.add_argument("--queues", type=int, default=8, help="work queues of the single launch (1 or 8)")
     ap.add_argument("--copy-chunk", type=int, default=2 << 20, help="bytes per copy item of the single launch")
-    ap.add_argument("--copy-ahead", type=int, default=4, help="copy lookahead of the single launch (groups)")
+    ap.add_argument("--copy-ahead", type=int, default=1,
+                    help="segments of the single launch whose tiles claim a copy quota before their GEMM")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")

@@ -224,7 +224,9 @@ struct dist_gemm_plan_s {
   uint64_t* d_times = nullptr;           // [step_timing][timeline_words(S)]
   uint64_t fused_align = 0;   // OR of the piece sizes (copy unit choice)
   int n_segs = 0;             // segments in the device tables
-  int copy_ahead = 4;         // copy lookahead, segments
+  int n_list0 = 0, n_list1 = 0, n_local = 0;  // copy pieces: of claim lists 0 and 1; of step 0
+  bool fused_loop = false;                    // list-1 pieces are copied inside K loops
+  int copy_ahead = 1;         // segments whose tiles claim a copy quota before their GEMM
   bool captured = false;      // a run was captured into a graph: tables are fixed
   std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
@@ -537,7 +539,7 @@ int alloc_fused(dist_gemm_plan_s* P, std::string* err) {
   const size_t n_sync = static_cast<size_t>(dg::sync_words(S));
   DG_HIP(err, hipMalloc(&P->d_segs, sizeof(dg::FusedSeg) * S));
   DG_HIP(err, hipMalloc(&P->d_copies, sizeof(dg::FusedStepCopy) * S));
-  DG_HIP(err, hipMalloc(&P->d_strips, sizeof(int32_t) * 2 * P->n_strips));
+  DG_HIP(err, hipMalloc(&P->d_strips, sizeof(int32_t) * (2 * P->n_strips + S)));
   DG_HIP(err, hipMalloc(&P->d_seg, sizeof(int32_t) * dg::kMaxQueues * (S + 1)));
   DG_HIP(err, hipMalloc(&P->d_ctr, sizeof(uint32_t) * n_ctr));
   DG_HIP(err, hipMalloc(&P->d_sync, sizeof(int32_t) * n_sync));
@@ -555,7 +557,9 @@ int alloc_fused(dist_gemm_plan_s* P, std::string* err) {
 struct FusedTables {
   std::vector<dg::FusedSeg> segs;
   std::vector<dg::FusedStepCopy> copies;
-  std::vector<int32_t> strips;  // strip list, then the step of each position
+  std::vector<int32_t> strips;  // strip list, the step of each position, the steps in claim order
+  int32_t n_list0 = 0, n_list1 = 0, n_local = 0;  // pieces: of lists 0 and 1; of step 0
+  bool loop = false;                               // list-1 pieces are copied inside K loops
   std::vector<int32_t> seg;     // [nq][n_segs + 1]
   uint64_t align = 0;           // OR of the contiguous piece sizes
 };
@@ -563,8 +567,9 @@ struct FusedTables {
 struct FusedOpts {
   int queues = dg::kMaxQueues;
   int64_t copy_chunk = 2 << 20;
-  int copy_ahead = 4;
+  int copy_ahead = 1;
   int max_group = 2;
+  int n_wg = 256;  // workgroups of the launch
 };
 
 int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, const FusedOpts& o,
@@ -609,71 +614,86 @@ int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, c
     f.strip0 = sfirst[segr[g].first];
     f.nst = sfirst[segr[g].second + 1] - f.strip0;
     f.tiles = static_cast<int32_t>(f.nst * other);
-    f.carry_first = f.claim_first = S;
-    f.carry_last = f.claim_last = -1;
+    f.quota = 0;
     for (int h = segr[g].first; h <= segr[g].second; ++h) seg_of[h] = g;
     if (static_cast<int64_t>(f.nst) * other * L >= INT32_MAX)
       return fail(err, DIST_GEMM_ERR_SHAPE, "too many tiles for one launch");
   }
-  // carriers: the latest segment with tiles at least D before the step's,
-  // else the first one before it, else the step's own tiles claim its copy
+  // Copies.  Every staged strip (and, for a returned gathered image, every
+  // strip of step 0) is cut into pieces, numbered in claim order: list 0
+  // (steps 1 .. h1, which the first round of tiles reads), list 1 (steps
+  // h1+1 .. S-1), then step 0.  List 0 is claimed before any GEMM: a quota
+  // by every tile of the first COPY_AHEAD segments, the rest by the first
+  // round's waiting tiles.  In-loop form: list 0 in pieces of 128 KiB; a
+  // tile that starts its GEMM copies one piece of list 1 inside its K loop
+  // (16 KiB per slab over at most its KT - 2 steady-state slabs), pieces
+  // being a strip's equal share, no larger than that and as small as the
+  // deadlines allow (the pieces of steps up to h are claimed by tiles that
+  // start before step h's segment can: n_wg per round), down to 64 KiB.
+  // Quota form (column strips, rows not 16-byte multiples, fewer than 6
+  // slabs, COPY_AHEAD 0, or no step after h1): list 1 is empty, pieces of
+  // about a quarter of the copy bytes per claimer (whole 32 KiB above that,
+  // at least 4 KiB, at most COPY_CHUNK bytes).
+  const int64_t per_q = std::max(1, o.n_wg / nq);  // the first round: the first per_q items of every queue
+  auto items_of = [&](int g, int q) -> int64_t {
+    return (segs[g].tiles / nq + (q < segs[g].tiles % nq ? 1 : 0)) * L;
+  };
+  std::vector<int64_t> seg_round(G, INT64_MAX);  // the earliest round a tile of segment g starts in
+  int g_first = 0;                               // the last segment the first round reaches
+  int64_t carriers = 0, waiters = 0;             // claimers of list 0
+  for (int q = 0; q < nq; ++q) {
+    int64_t at = 0;
+    for (int g = 0; g < G; ++g) {
+      const int64_t items = items_of(g, q);
+      if (items == 0) continue;
+      seg_round[g] = std::min(seg_round[g], at / per_q);
+      if (at < per_q) {
+        g_first = std::max(g_first, g);
+        if (g >= o.copy_ahead) waiters += std::min(items, per_q - at);
+      }
+      at += items;
+    }
+  }
+  for (int g = 0; g < G && g < o.copy_ahead; ++g) carriers += static_cast<int64_t>(segs[g].tiles) * L;
+  const int64_t claimers = std::max<int64_t>(1, carriers + waiters);
+  const int h1 = segr[g_first].second;
+  const int64_t KT = (pr.K * pr.es_in + dg::kRowBytes - 1) / dg::kRowBytes;
+  const int64_t cap = std::max<int64_t>(0, KT - 2) * dg::kLoopCopyBytes;
+  const bool loop = !sg.strided && sg.row_bytes % 16 == 0 && o.copy_ahead >= 1 && cap >= 4 * dg::kLoopCopyBytes &&
+                    h1 < S - 1;
+  int64_t piece0, piece1;
+  if (loop) {
+    piece0 = std::min<int64_t>(sg.strip_bytes, 131072);
+    const int64_t n_min = (sg.strip_bytes + cap - 1) / cap;
+    const int64_t n_small = (sg.strip_bytes + 65535) / 65536;
+    int64_t n_dead = n_small, cum = 0;
+    for (int h = h1 + 1; h < S; ++h) {
+      cum += static_cast<int64_t>(sfirst[h + 1] - sfirst[h]) * sg.LG;
+      const int64_t r = seg_round[seg_of[h]];
+      if (cum > 0 && r != INT64_MAX) n_dead = std::min(n_dead, o.n_wg * r / cum);
+    }
+    const int64_t n = std::max(n_min, std::min(n_dead, n_small));
+    piece1 = std::min(cap, ((sg.strip_bytes + n - 1) / n + 4095) / 4096 * 4096);
+  } else {
+    int64_t staged_strips = 0;
+    for (int h = 1; h < S; ++h) staged_strips += sfirst[h + 1] - sfirst[h];
+    const int64_t copy_bytes = std::max<int64_t>(1, staged_strips) * sg.LG * sg.strip_bytes;
+    int64_t piece = (copy_bytes + 4 * claimers - 1) / (4 * claimers);
+    piece = std::max<int64_t>(4096, (piece + 15) / 16 * 16);
+    if (piece > 32768) piece = (piece + 32767) / 32768 * 32768;
+    piece0 = piece1 = std::min<int64_t>(o.copy_chunk, piece);
+  }
   std::vector<dg::FusedStepCopy> cps(S);
-  for (int h = 0; h < S; ++h) {
+  std::vector<int32_t> order;  // steps in claim order
+  for (int h = 1; h < S; ++h) order.push_back(h);
+  order.push_back(0);
+  int64_t n_list0 = 0, n_list1 = 0, base = 0;
+  for (int h : order) {
     dg::FusedStepCopy& c = cps[h];
     c.strip0 = sfirst[h];
     c.nst = sfirst[h + 1] - sfirst[h];
     c.wait = h >= 1 ? 1 : 0;
-    c.P = 1;
-    c.piece = sg.strip_bytes;
-    c.n_chunks = 0;
-    if (c.nst == 0) continue;
-    int carrier = -1;
-    bool claim = false;
-    if (h == 0) {
-      carrier = 0;  // step 0's tiles never wait: they may carry their own strips
-    } else {
-      const int sh = seg_of[h];
-      for (int g = sh - o.copy_ahead; g >= 0 && carrier < 0; --g)
-        if (segs[g].tiles > 0) carrier = g;
-      for (int g = 0; g < sh && carrier < 0; ++g)
-        if (segs[g].tiles > 0) carrier = g;
-      if (carrier < 0) {
-        carrier = sh;
-        claim = true;
-      }
-    }
-    dg::FusedSeg& cs = segs[carrier];
-    if (claim) {
-      cs.claim_first = std::min(cs.claim_first, h);
-      cs.claim_last = std::max(cs.claim_last, h);
-    } else {
-      cs.carry_first = std::min(cs.carry_first, h);
-      cs.carry_last = std::max(cs.carry_last, h);
-    }
-    // pieces: about four per carrier tile over all the steps the carrier
-    // segment carries (so balanced contiguous ranges differ by a quarter at
-    // most), whole 32 KiB batches of the copy loop above that size, at
-    // least 4 KiB, at most COPY_CHUNK bytes
-    const int64_t ctiles = std::max<int64_t>(1, static_cast<int64_t>(cs.tiles) * L);
-    int64_t carried = 0;
-    for (int h2 = 0; h2 < S; ++h2) {
-      const int n2 = sfirst[h2 + 1] - sfirst[h2];
-      if (n2 == 0 || h2 == 0) continue;
-      int c2 = -1;
-      const int sh2 = seg_of[h2];
-      for (int g = sh2 - o.copy_ahead; g >= 0 && c2 < 0; --g)
-        if (segs[g].tiles > 0) c2 = g;
-      for (int g = 0; g < sh2 && c2 < 0; ++g)
-        if (segs[g].tiles > 0) c2 = g;
-      if (c2 < 0) c2 = sh2;
-      if (c2 == carrier) carried += n2;
-    }
-    if (h == 0) carried += c.nst;
-    const int64_t total = std::max<int64_t>(carried, c.nst) * sg.LG * sg.strip_bytes;
-    int64_t piece = (total + 4 * ctiles - 1) / (4 * ctiles);
-    piece = std::max<int64_t>(4096, (piece + 15) / 16 * 16);
-    if (piece > 32768) piece = (piece + 32767) / 32768 * 32768;
-    piece = std::min<int64_t>(o.copy_chunk, piece);
+    const int64_t piece = (loop && (h > h1 || h == 0)) ? piece1 : piece0;
     int64_t per;
     if (!sg.strided) {
       c.piece = piece;
@@ -683,13 +703,16 @@ int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, c
       per = (sg.height + c.piece - 1) / c.piece;
     }
     const int64_t n = per * c.nst * sg.LG;
-    if (n > (int64_t{1} << 30))
+    if (base + n > (int64_t{1} << 30))
       return fail(err, DIST_GEMM_ERR_UNSUPPORTED, "too many copy pieces; raise DIST_GEMM_OPT_COPY_CHUNK");
     c.P = static_cast<int32_t>(per);
     c.n_chunks = static_cast<int32_t>(n);
+    c.base = static_cast<int32_t>(base);
+    base += n;
+    if (h != 0) ((loop && h > h1) ? n_list1 : n_list0) += n;
   }
-  // (the carrier segment does not decrease with the step, so every segment
-  // carries a contiguous range of steps, and claims only steps of its own)
+  const int64_t quota = (n_list0 + claimers - 1) / claimers;
+  for (int g = 0; g < G && g < o.copy_ahead; ++g) segs[g].quota = static_cast<int32_t>(quota);
   // queue q: its share of every segment's tiles (a contiguous range of the
   // segment's tile order per batch), segment after segment
   std::vector<int32_t> seg(static_cast<size_t>(nq) * (G + 1), 0);
@@ -705,6 +728,11 @@ int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, c
   }
   out->strips = list;
   out->strips.insert(out->strips.end(), lstep.begin(), lstep.end());
+  out->strips.insert(out->strips.end(), order.begin(), order.end());
+  out->n_list0 = static_cast<int32_t>(n_list0);
+  out->n_list1 = static_cast<int32_t>(n_list1);
+  out->n_local = static_cast<int32_t>(base - n_list0 - n_list1);
+  out->loop = loop;
   out->segs = std::move(segs);
   out->copies = std::move(cps);
   out->seg = std::move(seg);
@@ -720,6 +748,7 @@ FusedOpts plan_opts(const dist_gemm_plan_s* P) {
   o.copy_chunk = P->copy_chunk;
   o.copy_ahead = P->copy_ahead;
   o.max_group = P->max_group;
+  o.n_wg = std::max(P->queues, P->n_cu / P->queues * P->queues);
   return o;
 }
 
@@ -735,6 +764,10 @@ int build_fused(dist_gemm_plan_s* P, std::string* err) {
   DG_HIP(err, hipMemcpy(P->d_seg, t.seg.data(), t.seg.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   P->n_segs = static_cast<int>(t.segs.size());
   P->fused_align = t.align;
+  P->n_list0 = t.n_list0;
+  P->n_list1 = t.n_list1;
+  P->n_local = t.n_local;
+  P->fused_loop = t.loop;
   return DIST_GEMM_OK;
 }
 
@@ -754,12 +787,14 @@ FusedOrder& fused_order() {
 struct FusedDevice {
   const dg::FusedSeg* segs;
   const dg::FusedStepCopy* copies;
-  const int32_t* strips;  // list, then steps
+  const int32_t* strips;  // list, steps of the positions, steps in claim order
   const int32_t* seg;
   uint32_t* ctr;
   int32_t* sync;
   int n_strips, n_segs;
   uint64_t piece_align;
+  int n_list0, n_list1, n_local;  // pieces: of claim lists 0 and 1; of step 0
+  bool loop;                      // list-1 pieces are copied inside K loops
 };
 
 // Arguments of one single-launch run of the problem pr.
@@ -783,6 +818,7 @@ dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, c
   a.steps = dv.copies;
   a.strip_list = dv.strips;
   a.strip_step = dv.strips + dv.n_strips;
+  a.claim_steps = dv.strips + 2 * dv.n_strips;
   a.seg = dv.seg;
   a.sync = dv.sync;
   a.ctr = dv.ctr;
@@ -809,6 +845,23 @@ dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, c
   a.S = pr.S;
   a.copy_on = copy_on ? 1 : 0;
   a.copy_local = copy_local ? 1 : 0;
+  // step 0's pieces (copy_local) close the last list in use
+  const int nz = copy_local ? dv.n_local : 0;
+  if (!copy_on) {
+    a.list_begin[0] = a.list_end[0] = a.list_begin[1] = a.list_end[1] = 0;
+  } else if (dv.n_list1 > 0) {
+    a.list_begin[0] = 0;
+    a.list_end[0] = dv.n_list0;
+    a.list_begin[1] = dv.n_list0;
+    a.list_end[1] = dv.n_list0 + dv.n_list1 + nz;
+  } else {
+    a.list_begin[0] = 0;
+    a.list_end[0] = dv.n_list0 + nz;
+    a.list_begin[1] = a.list_end[1] = a.list_end[0];
+  }
+  // the in-loop copy moves whole 16-byte units (else the list-1 pieces go to
+  // waiting and finished workgroups)
+  a.loop_copy = copy_on && dv.loop && dv.n_list1 > 0 && a.unit == 16 ? 1 : 0;
   return a;
 }
 
@@ -846,7 +899,7 @@ int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B,
               bool copy_local, uint64_t* times, uint64_t* times_next) {
   const Problem& pr = P->pr;
   FusedDevice dv{P->d_segs, P->d_copies, P->d_strips, P->d_seg, P->d_ctr, P->d_sync,
-                 P->n_strips, P->n_segs, P->fused_align};
+                 P->n_strips, P->n_segs, P->fused_align, P->n_list0, P->n_list1, P->n_local, P->fused_loop};
   dg::FusedArgs a = fused_args(pr, dv, P->queues, A, B, C, D, P->bias, G, alpha, beta, P->result_scale,
                                copy_src, copy_on, copy_local, P->wait_limit_us * P->clock_khz / 1000,
                                P->copy_delay_us * P->clock_khz / 1000);
@@ -899,15 +952,15 @@ constexpr size_t kNaSegs = 0, kNaCopies = 1024, kNaStrips = 2048, kNaSeg = 4096,
                  kNaCtr = 16384;
 static_assert(sizeof(dg::FusedSeg) * kNoAllocMaxSteps <= kNaCopies - kNaSegs, "no-alloc layout");
 static_assert(sizeof(dg::FusedStepCopy) * kNoAllocMaxSteps <= kNaStrips - kNaCopies, "no-alloc layout");
-static_assert(sizeof(int32_t) * 2 * kNoAllocMaxStrips <= kNaSeg - kNaStrips, "no-alloc layout");
-static_assert(sizeof(int32_t) * dg::kMaxQueues * (kNoAllocMaxSteps + 1) <= kNaSync - kNaSeg, "no-alloc layout");
-static_assert(sizeof(int32_t) * (dg::kSyncClaim + kNoAllocMaxSteps) * dg::kSyncStride <= kNaCtr - kNaSync,
+static_assert(sizeof(int32_t) * (2 * kNoAllocMaxStrips + kNoAllocMaxSteps) <= kNaSeg - kNaStrips,
               "no-alloc layout");
+static_assert(sizeof(int32_t) * dg::kMaxQueues * (kNoAllocMaxSteps + 1) <= kNaSync - kNaSeg, "no-alloc layout");
+static_assert(sizeof(int32_t) * (dg::kSyncClaim + 1) * dg::kSyncStride <= kNaCtr - kNaSync, "no-alloc layout");
 
 struct NoAllocPack {
   dg::FusedSeg segs[kNoAllocMaxSteps];
   dg::FusedStepCopy copies[kNoAllocMaxSteps];
-  int32_t strips[2 * kNoAllocMaxStrips];
+  int32_t strips[2 * kNoAllocMaxStrips + kNoAllocMaxSteps];
   int32_t seg[dg::kMaxQueues * (kNoAllocMaxSteps + 1)];
   int32_t n_segs, n_strips, S, n_ctr;
 };
@@ -925,7 +978,8 @@ __global__ __launch_bounds__(256) void noalloc_setup_kernel(NoAllocPack pk, uint
     reinterpret_cast<dg::FusedSeg*>(tables + kNaSegs)[i] = pk.segs[i];
   for (int i = t; i < pk.S; i += 256)
     reinterpret_cast<dg::FusedStepCopy*>(tables + kNaCopies)[i] = pk.copies[i];
-  for (int i = t; i < 2 * pk.n_strips; i += 256) reinterpret_cast<int32_t*>(tables + kNaStrips)[i] = pk.strips[i];
+  for (int i = t; i < 2 * pk.n_strips + pk.S; i += 256)
+    reinterpret_cast<int32_t*>(tables + kNaStrips)[i] = pk.strips[i];
   for (int i = t; i < dg::kMaxQueues * (pk.n_segs + 1); i += 256)
     reinterpret_cast<int32_t*>(tables + kNaSeg)[i] = pk.seg[i];
   for (int i = t; i < dg::sync_words(pk.S); i += 256) reinterpret_cast<int32_t*>(tables + kNaSync)[i] = 0;
@@ -1154,8 +1208,8 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
       return change_tables(plan, [&] { plan->copy_chunk = value; }, [&] { plan->copy_chunk = old; });
     }
     case DIST_GEMM_OPT_COPY_AHEAD: {
-      if (value < 1 || value > 64)
-        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy lookahead must be 1..64");
+      if (value < 0 || value > 64)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy-ahead segments must be 0..64");
       if (plan->copy_ahead == value) return DIST_GEMM_OK;
       const int old = plan->copy_ahead;
       return change_tables(plan, [&] { plan->copy_ahead = static_cast<int>(value); },
@@ -1536,7 +1590,9 @@ int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, in
     return DIST_GEMM_OK;
   }
   FusedTables t;
-  rc = compute_fused(pr, steps, FusedOpts{}, &t, nullptr);
+  FusedOpts fo;
+  fo.n_wg = std::max(dg::kMaxQueues, nd.n_cu / dg::kMaxQueues * dg::kMaxQueues);
+  rc = compute_fused(pr, steps, fo, &t, nullptr);
   if (rc != DIST_GEMM_OK) return rc;
   NoAllocPack pk{};
   for (size_t i = 0; i < t.segs.size(); ++i) pk.segs[i] = t.segs[i];
@@ -1552,7 +1608,7 @@ int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, in
                  reinterpret_cast<const dg::FusedStepCopy*>(tables + kNaCopies),
                  reinterpret_cast<const int32_t*>(tables + kNaStrips), reinterpret_cast<const int32_t*>(tables + kNaSeg),
                  reinterpret_cast<uint32_t*>(tables + kNaCtr), reinterpret_cast<int32_t*>(tables + kNaSync),
-                 n_strips, pk.n_segs, t.align};
+                 n_strips, pk.n_segs, t.align, t.n_list0, t.n_list1, t.n_local, t.loop};
   const bool copy_on = !(reduce_scatter(pr.schedule) && beta == 0.0f);
   const void* copy_src = pr.schedule == DIST_GEMM_AG_ROT_A ? A : pr.schedule == DIST_GEMM_AG_ROT_B ? B : C;
   const int64_t spin = int64_t{1000000} * nd.clock_khz / 1000;  // 1 s, as the plans' default

@@ -30,31 +30,38 @@
 // contiguous range of each segment's tile order, walked in groups of four
 // strips; nq = 1: one queue for the chip), in queue order, by an atomic
 // counter: queue q lists its tiles of segment 0 (step 0), then of segment
-// 1 (the next steps), and so on.  The shard copies ride on the tiles: the
-// copy of step h is cut into pieces of its strips, carried by the tiles of
-// an earlier segment (about D segments before h's, D = the copy lookahead),
-// and a tile performs the pieces it carries before it waits for anything
-// and before its own GEMM.  Equal pieces on every carrier keep the tiles of
-// an XCD in phase, so they share each K slab of A and B in the XCD's L2.
-// A step whose segment is the first with tiles has no earlier carrier: its
-// pieces are claimed at run time (an atomic counter) by its own tiles, each
-// of which claims until none are left before it waits.
+// 1 (the next steps), and so on.
 //
-// Progress.  A carrier does its pieces without waiting, and a tile waits
-// only for pieces carried by tiles of earlier segments, which precede it in
-// every queue, or claimed by tiles that do not wait before finishing them.
-// Take the lowest segment that any waiting workgroup waits for; every queue
-// with a waiting workgroup has handed out all its tiles of earlier segments,
-// and every other queue hands tiles out until it passes them; all of them
-// carry out their pieces.  So every wait ends, given that every queue keeps
-// at least one running workgroup (the host orders single-launch runs on a
+// Copies.  The staged strips are cut into pieces, numbered in step order
+// (steps 1 .. S-1, then the local step when the gathered image is
+// returned), and handed out by two atomic claim counters over consecutive
+// ranges of that order: list 0 holds the steps that tiles of the launch's
+// first round read, list 1 the later steps.  List 0 goes first, in small
+// pieces copied through LDS by every workgroup of the first round: the
+// tiles of the first segments (which read the local shard) claim a quota
+// before their GEMM, and a tile of a staged strip that is not yet complete
+// claims pieces one at a time while it waits (list 0, then list 1) instead
+// of spinning.  A tile that starts its GEMM claims one piece of list 1 and
+// copies it inside its K loop, where the copy's loads and stores ride in the
+// shadow of the MFMAs; list-1 pieces are sized so that the tiles starting
+// before a step's segment carry all of its pieces.  (Where a piece cannot be
+// copied inside the loop -- column strips, unaligned rows, too few slabs --
+// list 1 is empty and list 0 holds every staged step.)  Workgroups whose
+// queue is empty claim whatever is left.
+//
+// Progress.  A workgroup copies what it claims before it waits on
+// anything (an in-loop piece is claimed only once the tile's own wait is
+// over), and a waiting workgroup claims while pieces are left; once none
+// are left, every piece is held by a running workgroup that finishes it
+// without waiting.  So every wait ends, given that every queue keeps at
+// least one running workgroup (the host orders single-launch runs on a
 // device one after another).  Should a wait nevertheless outlast its limit
 // (another kernel holding CUs, say), the workgroup copies its strip itself
-// -- the same bytes the carriers write, so the duplicate is harmless, and
+// -- the same bytes the claimers write, so the duplicate is harmless, and
 // the strip's region of G is read by no tile that has already finished --
 // counts the event, and goes on with a correct result.
 //
-// Visibility.  Every wave of a carrier waits until its piece stores have
+// Visibility.  Every wave of a claimer waits until its piece stores have
 // reached L2; after a barrier thread 0 fences at agent scope (L2
 // write-back) and adds the pieces to their strips' counters; a waiting
 // thread polls the counter with agent-scope loads and then performs an
@@ -72,8 +79,6 @@
 
 namespace dg {
 namespace tile {
-
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 // Copy `rows` rows of `bytes` bytes (a multiple of sizeof(T)) from src to dst,
 // rows spitch / dpitch bytes apart, with the workgroup's 256 threads: batches
@@ -256,6 +261,44 @@ __device__ __forceinline__ int64_t item_rank(int i, int q, int T2, int L, int nq
   return before + same;
 }
 
+// The step whose pieces [base, base + n_chunks) of the claim order hold
+// piece p (claim_steps lists the steps in that order).
+__device__ __forceinline__ int piece_step(const FusedArgs& a, int p) {
+  int k = 0;
+  while (p >= a.steps[a.claim_steps[k]].base + a.steps[a.claim_steps[k]].n_chunks) ++k;
+  return a.claim_steps[k];
+}
+
+// Copy pieces [p0, p1) of the claim order with the whole workgroup, then
+// (thread 0) write them back and count them.  The first copy of a workgroup waits for the delay test hook.
+__device__ __forceinline__ void copy_claimed(const FusedArgs& a, int p0, int p1, uint8_t* smem,
+                                             bool& delayed, uint64_t t_start) {
+  if (!delayed) {
+    if (threadIdx.x == 0)
+      while (wall_clock64() - t_start < static_cast<uint64_t>(a.delay)) __builtin_amdgcn_s_sleep(8);
+    delayed = true;
+    barrier_only();
+  }
+  int k = 0;
+  for (int p = p0; p < p1; ++p) {
+    while (p >= a.steps[a.claim_steps[k]].base + a.steps[a.claim_steps[k]].n_chunks) ++k;
+    const FusedStepCopy& sh = a.steps[a.claim_steps[k]];
+    const ChunkAt at = chunk_at(a, sh, p - sh.base);
+    copy_piece(a, sh.piece, a.strip_list[at.pos], at.lg, at.piece, smem);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are in L2
+  barrier_only();
+  if (threadIdx.x == 0) {
+    __threadfence();  // write back the pieces, then count them
+    k = 0;
+    for (int p = p0; p < p1; ++p) {
+      while (p >= a.steps[a.claim_steps[k]].base + a.steps[a.claim_steps[k]].n_chunks) ++k;
+      const int h = a.claim_steps[k];
+      count_chunk(a, h, p - a.steps[h].base);
+    }
+  }
+}
+
 template <int IN, int OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 fused_run_kernel(FusedArgs a) {
@@ -269,6 +312,8 @@ fused_run_kernel(FusedArgs a) {
   int32_t* const qctr = a.sync + q * kSyncStride;
   int32_t* const nexit = a.sync + kSyncExit * kSyncStride;
   int32_t* const nerr = a.sync + kSyncErr * kSyncStride;
+  int32_t* const claim0 = a.sync + kSyncClaim * kSyncStride;
+  int32_t* const claim1 = a.sync + (kSyncClaim + 1) * kSyncStride;
   const int32_t* const seg = a.seg + q * (a.n_seg + 1);
   const int n_items = seg[a.n_seg];
   const uint64_t t_start = wall_clock64();
@@ -281,6 +326,9 @@ fused_run_kernel(FusedArgs a) {
   int acq_g = -1, acq_l = -1;
   uint64_t acq_steps = 0, acq_strips = 0;
   bool delayed = a.delay == 0;
+  // lists whose pieces are all handed out (uniform)
+  bool done0 = !a.copy_on || a.list_begin[0] >= a.list_end[0];
+  bool done1 = !a.copy_on || a.list_begin[1] >= a.list_end[1];
   int g = 0;  // segment of the last tile (tiles come in increasing order)
   for (;;) {
     barrier_only();  // every wave is done with the previous tile and its broadcast words
@@ -312,124 +360,114 @@ fused_run_kernel(FusedArgs a) {
     const FusedStepCopy& own = a.steps[h_own];
     const bool wait = a.copy_on && own.wait;
     const int lg = a.LG == 1 ? 0 : l;
-    // steps whose chunks this tile carries or claims (none when nothing rotates)
-    const int carry0 = a.copy_on ? (sg.carry_first == 0 && !a.copy_local ? 1 : sg.carry_first) : 1;
-    const int carry1 = a.copy_on ? sg.carry_last : 0;
-    const int claim0 = a.copy_on ? sg.claim_first : 1;
-    const int claim1 = a.copy_on ? sg.claim_last : 0;
 
-    // 1. the chunks this tile carries: the segment carries the steps
-    //    carry0..carry1, whose chunks form one list in step order; the
-    //    segment's tiles, ranked by the order in which they start, take
-    //    balanced contiguous ranges of it, so the earliest steps' copies are
-    //    done first.  Then, for a step without an earlier carrier, chunks
-    //    claimed until none are left.
-    if (!delayed && (carry0 <= carry1 || claim0 <= claim1)) {
-      if (tid == 0)
-        while (wall_clock64() - t_start < static_cast<uint64_t>(a.delay)) __builtin_amdgcn_s_sleep(8);
-      delayed = true;
-      barrier_only();
-    }
-    if (carry0 <= carry1) {
-      int64_t n = 0;
-      for (int h = carry0; h <= carry1; ++h) n += a.steps[h].n_chunks;
-      const int64_t rank = item_rank(i, q, T2, a.g.L, a.nq);
-      const int64_t p0 = rank * n / gtiles, p1 = (rank + 1) * n / gtiles;
-      if (p0 < p1) {
-        int h = carry0;
-        int64_t base = 0;
-        for (int64_t p = p0; p < p1; ++p) {
-          while (p - base >= a.steps[h].n_chunks) base += a.steps[h++].n_chunks;
-          const FusedStepCopy& sh = a.steps[h];
-          const ChunkAt at = chunk_at(a, sh, static_cast<int>(p - base));
-          copy_piece(a, sh.piece, a.strip_list[at.pos], at.lg, at.piece, smem);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are in L2
-        barrier_only();
-        if (tid == 0) {
-          __threadfence();  // write back the chunks, then count them
-          h = carry0;
-          base = 0;
-          for (int64_t p = p0; p < p1; ++p) {
-            while (p - base >= a.steps[h].n_chunks) base += a.steps[h++].n_chunks;
-            count_chunk(a, h, static_cast<int>(p - base));
-          }
-        }
-      }
-    }
-    for (int h = claim0; h <= claim1; ++h) {
-      const FusedStepCopy& sh = a.steps[h];
-      int32_t* const claim = a.sync + (kSyncClaim + h) * kSyncStride;
-      for (;;) {
-        barrier_only();
-        if (tid == 0) bcast[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        barrier_only();
-        const int c = __builtin_amdgcn_readfirstlane(bcast[1]);
-        if (c >= sh.n_chunks) break;
-        const ChunkAt at = chunk_at(a, sh, c);
-        copy_piece(a, sh.piece, a.strip_list[at.pos], at.lg, at.piece, smem);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        barrier_only();
-        if (tid == 0) {
-          __threadfence();
-          count_chunk(a, h, c);
-        }
-      }
-    }
-
-    // 2. a tile of a staged strip waits until the strip is complete
-    if (wait) {
-      if (tid == 0) {
-        int gave_up = 0;
-        if (acq_l != lg) {
-          acq_l = lg;
-          acq_steps = 0;
-          acq_g = -1;
-        }
-        if (acq_g != g) {
-          acq_g = g;
-          acq_strips = 0;
-        }
-        const bool known = (h_own < 64 && ((acq_steps >> h_own) & 1)) || (sp < 64 && ((acq_strips >> sp) & 1));
-        if (!known) {
-          const uint32_t P = static_cast<uint32_t>(own.P);
-          uint32_t* const ctr = strip_counter(a, lg, strip);
-          const uint64_t t0 = wall_clock64();
-          while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < P) {
-            if (wall_clock64() - t0 > static_cast<uint64_t>(a.spin_limit)) {
-              __hip_atomic_fetch_add(nerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              gave_up = 1;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-          if (!gave_up) {
-            // the whole step complete?  then the acquire below covers all of it
-            const uint32_t v = __hip_atomic_load(step_counter(a, lg, h_own), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            if (h_own < 64 && v >= P * static_cast<uint32_t>(own.nst))
-              acq_steps |= 1ull << h_own;
-            else if (sp < 64)
-              acq_strips |= 1ull << sp;
-          }
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
-        bcast[2] = gave_up;
-      }
+    // 1. the tiles of the first segments claim a quota of pieces before their
+    //    GEMM (the claim list is in step order, so the first claims copy the
+    //    first staged step)
+    if (sg.quota > 0 && !done0) {
+      if (tid == 0) bcast[1] = __hip_atomic_fetch_add(claim0, sg.quota, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       barrier_only();
-      if (__builtin_amdgcn_readfirstlane(bcast[2])) {
-        // the wait ran out: copy the strip here (the carriers' bytes exactly)
-        const int per = own.P;
-        for (int pc = 0; pc < per; ++pc) copy_piece(a, own.piece, strip, lg, pc, smem);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        barrier_only();
+      const int p0 = a.list_begin[0] + __builtin_amdgcn_readfirstlane(bcast[1]);
+      if (p0 >= a.list_end[0]) {
+        done0 = true;
+      } else {
+        copy_claimed(a, p0, min(p0 + sg.quota, a.list_end[0]), smem, delayed, t_start);
+        if (p0 + sg.quota >= a.list_end[0]) done0 = true;
+      }
+    }
+
+    // 2. a tile of a staged strip waits until the strip is complete; while it
+    //    is not and pieces are left, the workgroup claims and copies them one
+    //    at a time (a claimer copies before it waits on anything, so every
+    //    wait ends)
+    if (wait) {
+      for (;;) {
+        barrier_only();  // the broadcast words are free
         if (tid == 0) {
-          __threadfence();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          // 0: go on; 1: copy claimed piece bcast[1]; 2: the wait ran out
+          int state = 0;
+          if (acq_l != lg) {
+            acq_l = lg;
+            acq_steps = 0;
+            acq_g = -1;
+          }
+          if (acq_g != g) {
+            acq_g = g;
+            acq_strips = 0;
+          }
+          const bool known = (h_own < 64 && ((acq_steps >> h_own) & 1)) || (sp < 64 && ((acq_strips >> sp) & 1));
+          if (!known) {
+            const uint32_t P = static_cast<uint32_t>(own.P);
+            uint32_t* const ctr = strip_counter(a, lg, strip);
+            bool ready = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= P;
+            if (!ready && !done0) {
+              const int pc = a.list_begin[0] +
+                             __hip_atomic_fetch_add(claim0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (pc < a.list_end[0]) {
+                state = 1;
+                bcast[1] = pc;
+              }
+              if (pc + 1 >= a.list_end[0]) done0 = true;
+            }
+            if (!ready && state == 0 && !done1) {
+              const int pc = a.list_begin[1] +
+                             __hip_atomic_fetch_add(claim1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (pc < a.list_end[1]) {
+                state = 1;
+                bcast[1] = pc;
+              }
+              if (pc + 1 >= a.list_end[1]) done1 = true;
+            }
+            if (state == 0 && !ready) {
+              const uint64_t t0 = wall_clock64();
+              while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < P) {
+                if (wall_clock64() - t0 > static_cast<uint64_t>(a.spin_limit)) {
+                  __hip_atomic_fetch_add(nerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  state = 2;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+              }
+            }
+            if (state == 0) {
+              // the whole step complete?  then the acquire covers all of it
+              const uint32_t v = __hip_atomic_load(step_counter(a, lg, h_own), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+              if (h_own < 64 && v >= P * static_cast<uint32_t>(own.nst))
+                acq_steps |= 1ull << h_own;
+              else if (sp < 64)
+                acq_strips |= 1ull << sp;
+            }
+            if (state != 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          }
+          bcast[2] = state;
+          bcast[3] = (done0 ? 1 : 0) | (done1 ? 2 : 0);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         barrier_only();
+        const int state = __builtin_amdgcn_readfirstlane(bcast[2]);
+        const int dn = __builtin_amdgcn_readfirstlane(bcast[3]);
+        done0 = (dn & 1) != 0;
+        done1 = (dn & 2) != 0;
+        if (state == 1) {
+          const int pc = __builtin_amdgcn_readfirstlane(bcast[1]);
+          copy_claimed(a, pc, pc + 1, smem, delayed, t_start);
+          continue;
+        }
+        if (state == 2) {
+          // the wait ran out: copy the strip here (the claimers' bytes exactly)
+          const int per = own.P;
+          for (int pc = 0; pc < per; ++pc) copy_piece(a, own.piece, strip, lg, pc, smem);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          barrier_only();
+          if (tid == 0) {
+            __threadfence();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          }
+          barrier_only();
+        }
+        break;
       }
     }
 
@@ -445,27 +483,91 @@ fused_run_kernel(FusedArgs a) {
     }
     const int tm = a.cols ? ob : strip;
     const int tn = a.cols ? strip : ob;
-    gemm_tile<IN, OUT>(gp, l, tm, tn, smem);
+    // the tile's in-loop piece (list 1), claimed now that its wait is over
+    LoopCopy lc;
+    lc.chunks = 0;
+    int lp_step = 0, lp_chunk = 0;
+    if (a.loop_copy && !done1) {
+      if (tid == 0) bcast[5] = __hip_atomic_fetch_add(claim1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_only();
+      const int pc = a.list_begin[1] + __builtin_amdgcn_readfirstlane(bcast[5]);
+      if (pc + 1 >= a.list_end[1]) done1 = true;
+      if (pc < a.list_end[1]) {
+        lp_step = piece_step(a, pc);
+        const FusedStepCopy& sh = a.steps[lp_step];
+        lp_chunk = pc - sh.base;
+        const ChunkAt at = chunk_at(a, sh, lp_chunk);
+        const int64_t r0 = static_cast<int64_t>(a.strip_list[at.pos]) * kBM;
+        const int64_t off = r0 * a.row_bytes + static_cast<int64_t>(at.piece) * sh.piece;
+        const int64_t end = min(r0 + kBM, a.ext) * a.row_bytes;
+        if (off < end) {
+          const int64_t bytes = min(sh.piece, end - off);
+          const int64_t o = static_cast<int64_t>(at.lg) * a.gbatch + off;
+          lc.src = a.src + o;
+          lc.dst = const_cast<uint8_t*>(a.gath) + o;
+          lc.bytes = static_cast<uint32_t>(bytes);
+          lc.chunks = static_cast<int>((bytes + kLoopCopyChunk - 1) / kLoopCopyChunk);
+        }
+        if (!delayed) {
+          if (tid == 0)
+            while (wall_clock64() - t_start < static_cast<uint64_t>(a.delay)) __builtin_amdgcn_s_sleep(8);
+          delayed = true;
+          barrier_only();
+        }
+        if (lc.chunks == 0 && tid == 0) count_chunk(a, lp_step, lp_chunk);  // an empty piece
+      }
+    }
+    // the piece's stores have reached L2 in every wave: write them back and count the piece
+    const auto after_loop = [&]() {
+      if (lc.chunks > 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier_only();
+        if (tid == 0) {
+          __threadfence();
+          count_chunk(a, lp_step, lp_chunk);
+        }
+      }
+    };
+    gemm_tile<IN, OUT, true>(gp, l, tm, tn, smem, &lc, after_loop);
     if (a.times && tid == 0)
       __hip_atomic_fetch_max(a.times + 3 + 3 * h_own, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Pieces nobody has claimed yet (the local shard's pieces of a returned
+  // gathered image, which no tile waits for): the workgroups whose queue is
+  // empty take them, a few at a time.
+  for (int li = 0; li < 2; ++li) {
+    bool done = li == 0 ? done0 : done1;
+    int32_t* const ctr = li == 0 ? claim0 : claim1;
+    while (!done) {
+      constexpr int kSweep = 4;
+      barrier_only();  // every wave has read the broadcast words
+      if (tid == 0) bcast[1] = __hip_atomic_fetch_add(ctr, kSweep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_only();
+      const int p0 = a.list_begin[li] + __builtin_amdgcn_readfirstlane(bcast[1]);
+      if (p0 >= a.list_end[li]) break;
+      copy_claimed(a, p0, min(p0 + kSweep, a.list_end[li]), smem, delayed, t_start);
+      done = p0 + kSweep >= a.list_end[li];
+    }
   }
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
     __threadfence();
     const int old = __hip_atomic_fetch_add(nexit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bcast[3] = old == static_cast<int>(gridDim.x) - 1;
+    bcast[4] = old == static_cast<int>(gridDim.x) - 1;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier_only();
-  if (bcast[3]) {
+  if (bcast[4]) {
     const int n = a.LG * (a.n_strips + a.S);
     for (int x = tid; x < n; x += kThreads)
       __hip_atomic_store(a.ctr + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) {
       for (int x = 0; x < a.nq; ++x)
         __hip_atomic_store(a.sync + x * kSyncStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int h = 0; h < a.S; ++h)
-        __hip_atomic_store(a.sync + (kSyncClaim + h) * kSyncStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(claim0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(claim1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(nexit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (a.times_next)

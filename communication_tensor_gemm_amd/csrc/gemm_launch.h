@@ -31,6 +31,10 @@ struct GemmParams {
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kRowBytes = 128;
+// Bytes a workgroup of the persistent kernel copies per K slab inside its K
+// loop (four waves, four 1 KiB loads each); a tile of KT slabs copies at
+// most KT - 2 such chunks.
+constexpr int kLoopCopyBytes = 16384;
 
 inline int in_elem_size(int in_kind) { return in_kind == IN_F32 ? 4 : (in_kind == IN_BF16 ? 2 : 1); }
 inline int out_elem_size(int out_kind) { return out_kind == OUT_F32 ? 4 : (out_kind == OUT_BF16 ? 2 : 1); }
@@ -49,18 +53,23 @@ inline int out_elem_size(int out_kind) { return out_kind == OUT_F32 ? 4 : (out_k
 // Work items are the tiles.  Workgroup b takes them from queue b mod nq, in
 // queue order, by an atomic counter; the queue order is by segment (step 0,
 // then groups of consecutive staged steps), each segment's tiles split into
-// nq contiguous ranges of its tile order.  The copy of step h is cut into
-// chunks (pieces of its strips) carried by the tiles of an earlier segment,
-// which copy them before their own GEMM; a tile of a staged strip waits
-// until every piece of that strip is done.  Pointers are not stored in the
-// tables; per-run pointers travel in FusedArgs.
+// nq contiguous ranges of its tile order.  The copies are pieces of the
+// staged strips, numbered in step order (steps 1 .. S-1, then step 0, whose
+// strips are copied only when the gathered image is returned) and handed out
+// by two atomic claim counters over two consecutive ranges of that order:
+// list 0, the steps the launch's first round of tiles reads, and list 1, the
+// later steps.  A tile of a staged strip claims and copies pieces (list 0,
+// then list 1) while its strip is incomplete; a tile that starts its GEMM
+// claims one piece of list 1 and copies it inside its K loop; in the quota
+// form (no in-loop copy), list 1 is empty and the tiles of the first
+// segments claim a quota of list 0 before their GEMM.  Pointers are not
+// stored in the tables; per-run pointers travel in FusedArgs.
 
 // One queue segment: consecutive steps whose tiles are ordered together.
 struct FusedSeg {
-  int32_t strip0, nst;               // its strips: positions strip0 .. strip0 + nst - 1
-  int32_t tiles;                     // tiles of one batch: nst * other_tiles
-  int32_t carry_first, carry_last;   // steps whose chunks its tiles carry (first > last: none)
-  int32_t claim_first, claim_last;   // steps whose chunks its tiles claim at run time
+  int32_t strip0, nst;  // its strips: positions strip0 .. strip0 + nst - 1
+  int32_t tiles;        // tiles of one batch: nst * other_tiles
+  int32_t quota;        // pieces each of its tiles claims before its GEMM (0: none)
 };
 
 // The copy of one step: its strips and their pieces.
@@ -68,22 +77,22 @@ struct FusedStepCopy {
   int64_t piece;        // bytes (row strips) or rows (column strips) per piece
   int32_t strip0, nst;  // its strips: positions in the strip list
   int32_t P;            // pieces per strip (the target of each strip's counter)
-  int32_t n_chunks;     // nst * LG * P when the step's strips are copied, else 0
+  int32_t n_chunks;     // nst * LG * P (its pieces)
   int32_t wait;         // its tiles wait for their strip and read the gathered image
-  int32_t pad;
+  int32_t base;         // index of its first piece in the claim order
 };
 
 // Synchronisation words (int32, one 128-byte line each), zero between runs
 // except the error count:
 //   [q] queue counters, q < nq;  [kSyncExit] workgroups finished;
 //   [kSyncErr] timed-out waits (never reset by a run);
-//   [kSyncClaim + h] chunks of step h claimed at run time.
+//   [kSyncClaim + i] pieces claimed from list i.
 constexpr int kSyncStride = 32;
 constexpr int kMaxQueues = 8;
 constexpr int kSyncExit = kMaxQueues;
 constexpr int kSyncErr = kMaxQueues + 1;
 constexpr int kSyncClaim = kMaxQueues + 2;
-__host__ __device__ inline int sync_words(int S) { return (kSyncClaim + S) * kSyncStride; }
+__host__ __device__ inline int sync_words(int /*S*/) { return (kSyncClaim + 2) * kSyncStride; }
 
 // Device timeline of one run (unsigned 64-bit wall-clock ticks), written
 // with atomic max only: [0] = ~(first workgroup start); per step s,
@@ -100,6 +109,7 @@ struct FusedArgs {
   const FusedStepCopy* steps;    // [S]
   const int32_t* strip_list;     // strips, step by step
   const int32_t* strip_step;     // step of each strip-list position
+  const int32_t* claim_steps;    // the steps in claim order
   const int32_t* seg;            // [nq][n_seg + 1]: first item of segment g in queue q
   int32_t* sync;
   uint32_t* ctr;                 // [LG][n_strips] pieces done per strip, then [LG][S] per
@@ -122,6 +132,9 @@ struct FusedArgs {
   int32_t n_seg, nq, S;
   int32_t copy_on;               // 0: nothing rotates (a reduce-scatter with beta = 0)
   int32_t copy_local;            // 1: step 0's strips are copied into G too (G is returned)
+  int32_t list_begin[2];         // claim lists this run: pieces [begin, end) of the claim order
+  int32_t list_end[2];           // (step 0's pieces at the end of the last list when copy_local)
+  int32_t loop_copy;             // 1: starting tiles copy a list-1 piece in their K loop
 };
 
 // Enqueue the single-launch run on `stream` with `grid` workgroups (a

@@ -60,6 +60,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kThreads = 256;
 constexpr int kSlab = 128;                        // bytes of K per operand row per slab
@@ -203,7 +204,9 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
 // fragment read q follows MFMA kReadAt + (q / kReadsPer) * kReadEvery and
 // DMA load d follows MFMA kDmaAt + d * kDmaEvery; both end early enough for
 // the reads to land before the next half slab and for the loads to keep
-// their lead.
+// their lead.  The persistent kernel's in-loop copy issues its four stores
+// after MFMA kCopyAt of the second half slab and its four loads after MFMA
+// kCopyAt + kCopyEvery, behind the operand DMA.
 template <int IN>
 struct Mma;
 
@@ -243,6 +246,7 @@ struct Mma<IN_BF16> : Mma16Base {
   // measured +1.4% on a 16384 x 13312 x 16384 TP=8 schedule
   static constexpr int kReadAt = 0, kReadEvery = 3, kReadsPer = 1;
   static constexpr int kDmaAt = 2, kDmaEvery = 6;
+  static constexpr int kCopyAt = 48, kCopyEvery = 8;
   // MFMA m: block (m / 8, m % 8)
   __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
     const int i = m >> 3, j = m & 7;
@@ -257,6 +261,7 @@ struct Mma<IN_F32> : Mma16Base {
   static constexpr int kMfma = 256;
   static constexpr int kReadAt = 1, kReadEvery = 4, kReadsPer = 1;
   static constexpr int kDmaAt = 2, kDmaEvery = 8;
+  static constexpr int kCopyAt = 96, kCopyEvery = 32;
   // MFMA m: K step t = m / 64 of block ((m / 8) % 8, m % 8).  The lane's 4
   // floats of a block are K values 4*(lane/16) + t; the 16x16x4 MFMA takes
   // lane group lane/16 as its K index, identically for A and B.
@@ -305,6 +310,7 @@ struct Mma<IN_E4M3> : Mma32Base {
   static constexpr int kMfma = 16;
   static constexpr int kReadAt = 0, kReadEvery = 1, kReadsPer = 2;
   static constexpr int kDmaAt = 0, kDmaEvery = 1;
+  static constexpr int kCopyAt = 9, kCopyEvery = 3;
   // MFMA m: block (m / 4, m % 4); format fields 0/0 select e4m3 for A and B
   __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NB][NB]) {
     const int i = m >> 2, j = m & 3;
@@ -372,12 +378,13 @@ __device__ __forceinline__ void issue_operand(const TileCtx& c, uint8_t* smem, i
 // One half slab: the MFMAs on Fm, with (kRead) the reads of the next half
 // slab into Fr from LDS bases ra / rb and (kIssue) the DMA of operand kOp of
 // slab kt_issue into ring slot slot_issue, in the type's fixed order.
-template <int IN, bool kIssue, bool kRead, int kOp>
+template <int IN, bool kIssue, bool kRead, int kOp, typename X>
 __device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int kt_issue,
                                           int slot_issue, const uint8_t* ra, const uint8_t* rb,
                                           const int (&fb)[4], const typename Mma<IN>::Frags& Fm,
                                           typename Mma<IN>::Frags& Fr,
-                                          typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB]) {
+                                          typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB],
+                                          const X& extra) {
   using M = Mma<IN>;
   const SlabLoad<kOp> L(c, smem, kt_issue, slot_issue);
 #pragma unroll
@@ -396,6 +403,7 @@ __device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int k
           if (g * M::kReadsPer + u < M::kReads) M::read(g * M::kReadsPer + u, ra, rb, fb, Fr);
       }
     }
+    extra(m);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -727,14 +735,46 @@ __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lan
   }
 }
 
+// A contiguous copy that a tile of the persistent kernel performs inside its
+// K loop, so that moving a shard costs memory operations in the shadow of
+// the MFMAs rather than CU time of its own: in steady-state slab kt every
+// wave stores the four 1 KiB it loaded in slab kt - 1 and loads chunk kt
+// (16 KiB per workgroup per slab), behind the slab's operand DMA.  The
+// loads land before the next slab's operand wait, which counts them with
+// the DMA loads they follow (vector-memory operations retire in order), and
+// the stores of slab kt retire before the wait of slab kt + 1 in the same
+// way.  A tile of KT slabs copies at most KT - 2 chunks; the descriptors
+// cover exactly the piece's bytes (a multiple of 16), so the last chunk's
+// lanes past its end neither read nor write.  Non-temporal: the bytes are
+// not reused by this tile.
+struct LoopCopy {
+  const uint8_t* src;
+  uint8_t* dst;
+  uint32_t bytes;
+  int chunks;  // 16 KiB chunks; 0: nothing to copy
+};
+constexpr int kLoopCopyOps = 4;                                    // 1 KiB loads per wave per slab
+constexpr int kLoopCopyChunk = kThreads / 64 * kLoopCopyOps * 1024;  // 16 KiB per workgroup per slab
+static_assert(kLoopCopyChunk == kLoopCopyBytes, "in-loop copy chunk");
+struct NoAfterLoop {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // One 256 x 256 tile (tm, tn) of batch l of the GEMM p, computed by the
 // whole workgroup with the LDS ring smem.  Every argument is workgroup-uniform.
-template <int IN, int OUT>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, int tn, uint8_t* smem) {
+// kCopy: the tile also performs the copy *lc inside its K loop and calls
+// after_loop() (with every wave) once the loop is done.
+template <int IN, int OUT, bool kCopy = false, typename AfterLoop = NoAfterLoop>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, int tn, uint8_t* smem,
+                                          const LoopCopy* lc = nullptr, const AfterLoop& after_loop = {}) {
   using M = Mma<IN>;
   constexpr int ES = elem_size<IN>();
 
-  const int lane = threadIdx.x & 63;
+  // the lane index, redefined per tile: in the persistent kernel, nothing
+  // derived from it is hoisted out of the tile loop (where it would hold
+  // VGPRs across every K loop)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = tm * kBM, n0 = tn * kBN;
@@ -785,6 +825,39 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
 
   typename M::Frags F0, F1;
 
+  // in-loop copy: a chunk's loads (stored one slab later) in cb; the
+  // descriptors cover the whole piece, lane offset cvoff within a chunk.
+  // Chunk j is loaded at slab j * stride and stored at the next slab, the
+  // stride spreading the piece's traffic over the loop.
+  u32x4 cb[kLoopCopyOps];
+  const uint32_t cvoff = static_cast<uint32_t>(wave) * (kLoopCopyOps * 1024) + static_cast<uint32_t>(lane) * 16;
+  const int n_chunks = kCopy ? __builtin_amdgcn_readfirstlane(lc->chunks) : 0;
+  const int stride = n_chunks > 0 ? max(1, (KT - 2) / n_chunks) : 1;
+  const __amdgpu_buffer_rsrc_t csrc = make_rsrc(kCopy ? lc->src : nullptr, kCopy ? lc->bytes : 0);
+  const __amdgpu_buffer_rsrc_t cdst = make_rsrc(kCopy ? lc->dst : nullptr, kCopy ? lc->bytes : 0);
+  int ld_j = 0, ld_at = 0;  // the next chunk to load and its slab
+  // after MFMA kCopyAt of a second half slab at slab kt: store the chunk
+  // loaded at slab kt - 1; after MFMA kCopyAt + kCopyEvery: load the next
+  // chunk if this is its slab
+  auto copy_ops = [&](int m, int kt_cur, bool loads) {
+    if constexpr (kCopy) {
+      if (m == M::kCopyAt && ld_j > 0 && kt_cur == ld_at - stride + 1) {
+        const uint32_t o = cvoff + static_cast<uint32_t>(ld_j - 1) * kLoopCopyChunk;
+#pragma unroll
+        for (int op = 0; op < kLoopCopyOps; ++op)
+          __builtin_amdgcn_raw_buffer_store_b128(cb[op], cdst, o + op * 1024, 0, 2);
+      }
+      if (m == M::kCopyAt + M::kCopyEvery && loads && ld_j < n_chunks && kt_cur == ld_at) {
+        const uint32_t o = cvoff + static_cast<uint32_t>(ld_j) * kLoopCopyChunk;
+#pragma unroll
+        for (int op = 0; op < kLoopCopyOps; ++op) cb[op] = __builtin_amdgcn_raw_buffer_load_b128(csrc, o + op * 1024, 0, 2);
+        ++ld_j;
+        ld_at += stride;
+      }
+    }
+  };
+  const auto none = [](int) {};
+
   // Prologue: A0, B0, A1, B1 into slots 0..3; slab 0 landed; its half 0 read.
   issue_operand<0>(c, smem, 0, 0);
   issue_operand<1>(c, smem, 0, 1);
@@ -812,31 +885,34 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   for (; kt + 2 < KT; ++kt) {
     wait_lgkmcnt0();
     half_step<IN, true, true, 0>(c, smem, kt + 2, slot_add(s, 4), smem + s * kOperandSlab + 512,
-                                 smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc);
+                                 smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc, none);
     wait_lgkmcnt0();
     wait_vmcnt<kLoadsPerOperand>();
     barrier_only();
     half_step<IN, true, true, 1>(c, smem, kt + 2, s, smem + slot_add(s, 2) * kOperandSlab,
-                                 smem + slot_add(s, 3) * kOperandSlab, fb, F1, F0, acc);
+                                 smem + slot_add(s, 3) * kOperandSlab, fb, F1, F0, acc,
+                                 [&](int m) { copy_ops(m, kt, true); });
     s = slot_add(s, 2);
   }
   if (kt + 1 < KT) {  // second to last slab: nothing left to prefetch
     wait_lgkmcnt0();
     half_step<IN, false, true, 0>(c, smem, kt, s, smem + s * kOperandSlab + 512,
-                                  smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc);
+                                  smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc, none);
     wait_lgkmcnt0();
     wait_vmcnt<0>();
     barrier_only();
     half_step<IN, false, true, 1>(c, smem, kt, s, smem + slot_add(s, 2) * kOperandSlab,
-                                  smem + slot_add(s, 3) * kOperandSlab, fb, F1, F0, acc);
+                                  smem + slot_add(s, 3) * kOperandSlab, fb, F1, F0, acc,
+                                  [&](int m) { copy_ops(m, kt, false); });
     s = slot_add(s, 2);
     ++kt;
   }
   wait_lgkmcnt0();  // last slab
   half_step<IN, false, true, 0>(c, smem, kt, s, smem + s * kOperandSlab + 512,
-                                smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc);
+                                smem + slot_add(s, 1) * kOperandSlab + 512, fb, F0, F1, acc, none);
   wait_lgkmcnt0();
-  half_step<IN, false, false, 1>(c, smem, kt, s, smem, smem, fb, F1, F0, acc);
+  half_step<IN, false, false, 1>(c, smem, kt, s, smem, smem, fb, F1, F0, acc, none);
+  if constexpr (kCopy) after_loop();
   // The MFMAs are opaque to the compiler's hazard tracking: give the last
   // ones their result latency, then redefine every accumulator after that
   // wait, so that no AGPR read of the epilogue can be scheduled above it (a

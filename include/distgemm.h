@@ -207,8 +207,11 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     0 = step launches and side-stream copies (the options above apply);
  *     1 (default) = one persistent launch on the caller's stream does
  *     the whole run on the monolithic tile grid: its workgroups take the
- *     tiles step by step, every tile first copying an equal piece of a
- *     later step's shard, and a tile that reads a staged shard starts once
+ *     tiles step by step and copy the staged shards in pieces handed out
+ *     in step order by device counters (a tile whose strip is not yet
+ *     complete copies pieces while it waits; a tile that starts its GEMM
+ *     copies one piece of a later step inside its K loop, see COPY_AHEAD),
+ *     and a tile that reads a staged shard starts once
  *     a device-side counter shows complete the strip it reads -- the 256
  *     rows (AG_ROT_A, RS_TILE_A_ROT_C) or columns (AG_ROT_B,
  *     RS_TILE_B_ROT_C) of the gathered operand that one tile row or column
@@ -222,25 +225,35 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *   DIST_GEMM_OPT_QUEUES (mode 1): 8 (default) = one work queue per XCD,
  *     each XCD runs contiguous ranges of every step's tile order; 1 = one
  *     queue for the chip.
- *   DIST_GEMM_OPT_COPY_CHUNK (mode 1): the largest copy piece one tile
- *     carries, in bytes, a multiple of 16 in [4096, 2^28]; default 2 MiB.
- *     A step's strips are spread over the tiles of the segment D before it
- *     in pieces of about equal size (step bytes / carrier tiles), capped by
- *     this.  The plan's device tables are rebuilt (synchronously) when it
- *     changes.
+ *   DIST_GEMM_OPT_COPY_CHUNK (mode 1, quota form below): the largest copy
+ *     piece, in bytes, a multiple of 16 in [4096, 2^28]; default 2 MiB.
+ *     Pieces are about a quarter of the copy bytes per claiming workgroup,
+ *     whole 32 KiB above that size, at least 4 KiB, capped by this (column
+ *     strips: whole rows of the strip).  The plan's device tables are
+ *     rebuilt (synchronously) when it changes.
  *   DIST_GEMM_OPT_WAIT_LIMIT_US (mode 1): how long one wait for a strip
  *     may last, in microseconds, in [0, 10^8]; default 10^6.  A wait that
  *     runs out is counted (dist_gemm_device_errors) and the waiting
  *     workgroup copies the strip into the gathered image itself (the same
- *     bytes its carriers write), so the result stays correct; it only costs
+ *     bytes its claimers write), so the result stays correct; it only costs
  *     time.  Waits run out when the launch cannot keep a workgroup running
  *     on every work queue (other kernels holding the device's CUs), never
  *     in an unshared device; 0 makes every wait copy its own strip.
- *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 1..64; the pieces of a step in
- *     segment h are carried by the tiles of the latest segment at or before
- *     h - D that has tiles (else the first segment that has), i.e. about D
- *     segments ahead of their use; default 4 (measured 0.5-2% faster than 2
- *     on the TP=8 workloads, where it puts every copy on step 0's tiles).
+ *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 0..64; default 1.  With D >= 1
+ *     and row strips (AG_ROT_A, AG_ROT_B, RS_TILE_A_ROT_C) whose rows are
+ *     a multiple of 16 bytes, K of at least 6 slabs (over 640 bytes of a row of
+ *     A) and steps left after those the launch's first round of tiles
+ *     reads: the in-loop form.  Every tile that starts its GEMM while
+ *     pieces of those later steps are left copies one inside its K loop
+ *     (16 KiB per 128-byte K slab, loads and stores behind the slab's
+ *     operand loads; a piece is an equal share of a strip no larger than
+ *     the tile's K loop carries), and the tiles of the first round that
+ *     wait copy the steps it reads.  Otherwise the quota form: every tile
+ *     of the first D segments claims a quota of copy pieces before its
+ *     GEMM (the staged pieces / (those tiles + the staged tiles of the
+ *     launch's first round)), and waiting tiles copy the rest.  In both,
+ *     workgroups with no tiles left copy whatever remains, and unaligned
+ *     operand or image pointers send in-loop pieces to those too.
  *   DIST_GEMM_OPT_SHARED_A: 1 = A holds one M x K matrix that every one of
  *     the L batches multiplies (B, C, D keep their L batches): the several-B
  *     form of the PyTorch symmetric-memory page's fused all-gather matmul

@@ -96,11 +96,13 @@ def test_single_launch_edges(M, N, K, TP, sched, dtype):
 
 @pytest.mark.parametrize("queues,chunk,group,ahead", [(8, 4096, 2, 2), (1, 4096, 1, 1), (1, 1 << 20, 3, 2),
                                                       (8, 16384, 1, 64), (8, 1 << 28, 7, 1),
-                                                      (8, 1 << 21, 1024, 3), (8, 4096, 1, 7)])
+                                                      (8, 1 << 21, 1024, 3), (8, 4096, 1, 7),
+                                                      (8, 8192, 2, 0), (1, 4096, 1, 0)])
 def test_single_launch_queues_chunks_groups(queues, chunk, group, ahead):
     """Work distribution does not change a bit of the result: one queue or
     one per XCD, chunks from 4 KiB (thousands of chunks) to one per shard,
-    launch groups from one step to all staged steps, copy lookahead 1 to all."""
+    launch groups from one step to all staged steps, quota-claiming segments
+    from none (waiting tiles copy everything) to all."""
     import torch
     for sched in ("AG_ROT_A", "AG_ROT_B", "RS_TILE_B_ROT_C"):
         w = workloads.small_case(f"fused_q{queues}_c{chunk}_g{group}_{sched}", sched, "BF16_F32", 1024,
@@ -243,7 +245,7 @@ def test_single_launch_option_errors():
     import communication_tensor_gemm_amd as dg
     with dg.Plan(512, 512, 64, 1, 2, "AG_ROT_A", "BF16_F32") as p:
         for opt, bad in (("EXECUTION", 2), ("QUEUES", 4), ("COPY_CHUNK", 4095), ("COPY_CHUNK", 4104),
-                         ("COPY_CHUNK", (1 << 28) + 16), ("WAIT_LIMIT_US", -1), ("COPY_AHEAD", 0),
+                         ("COPY_CHUNK", (1 << 28) + 16), ("WAIT_LIMIT_US", -1), ("COPY_AHEAD", -1),
                          ("COPY_AHEAD", 65)):
             with pytest.raises(dg.DistGemmError):
                 p.set_option(opt, bad)
