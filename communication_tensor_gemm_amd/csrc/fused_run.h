@@ -62,11 +62,12 @@
 // counts the event, and goes on with a correct result.
 //
 // Visibility.  Every wave of a claimer waits until its piece stores have
-// reached L2; after a barrier thread 0 fences at agent scope (L2
-// write-back) and adds the pieces to their strips' counters; a waiting
-// thread polls the counter with agent-scope loads and then performs an
-// agent-scope acquire (cache invalidate) before the barrier that releases
-// its workgroup into the tile.  Every piece also counts towards its step, so
+// reached L2; after a barrier thread 0 releases at agent scope (L2
+// write-back only: no invalidate, which would cost every tile on the XCD
+// its cached operand lines) and adds the pieces to their strips' counters;
+// a waiting thread polls the counter with agent-scope loads and then
+// performs an agent-scope acquire (cache invalidate) before the barrier
+// that releases its workgroup into the tile.  Every piece also counts towards its step, so
 // to keep acquires rare thread 0 reads, after its strip, the step's count
 // once: when the whole step is complete (the usual case, the copies run
 // ahead), the acquire covers every strip of the step and later tiles of the
@@ -131,17 +132,21 @@ __device__ __forceinline__ void copy_rows(const uint8_t* src, int64_t spitch, ui
 // workgroup's LDS, which is idle between tiles: each wave streams rounds of
 // 32 KiB straight into its own 32 KiB of LDS (buffer_load ... lds, 32
 // loads of 1 KiB in flight, no registers held while they fly), waits for
-// them, reads them back and stores them (non-temporal).  128 KiB per
-// workgroup in flight: the register-bounded loop above keeps 32 KiB, and
-// at HBM latency that bounds one CU's copy rate.  Loads past the end read
-// zeros (the buffer descriptor covers `bytes`) and are not stored.  The
-// caller passes a barrier before the LDS is used for anything else.
+// them, reads them back and stores them.  128 KiB per workgroup in flight:
+// the register-bounded loop above keeps 32 KiB, and at HBM latency that
+// bounds one CU's copy rate.  The buffer descriptors cover `bytes`: loads
+// past the end read zeros and stores past it are dropped.  The stores are
+// non-temporal and agent-coherent (cache policy nt sc1: written through to
+// where every XCD reads), so a release needs no L2 write-back for them.
+// The caller passes a barrier before the LDS is used for anything else.
+constexpr int kStoreAgentNT = 18;  // buffer store cache policy: sc1 (agent scope) | nt
 constexpr int kCopyWaveBytes = 32768;
 __device__ __forceinline__ void copy_lds(const uint8_t* src, uint8_t* dst, int64_t bytes, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   uint8_t* const lbase = smem + wave * kCopyWaveBytes;
   const __amdgpu_buffer_rsrc_t r = make_rsrc(src, static_cast<uint32_t>(bytes));
+  const __amdgpu_buffer_rsrc_t w = make_rsrc(dst, static_cast<uint32_t>(bytes));
   for (int64_t b0 = 0; b0 < bytes; b0 += 4 * kCopyWaveBytes) {
     const uint32_t wo = static_cast<uint32_t>(b0) + wave * kCopyWaveBytes + lane * 16;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the last round's reads are done
@@ -157,8 +162,7 @@ __device__ __forceinline__ void copy_lds(const uint8_t* src, uint8_t* dst, int64
         v[d] = *reinterpret_cast<const u32x4*>(lbase + 1024 * (d0 + d) + 16 * lane);
 #pragma unroll
       for (int d = 0; d < 8; ++d)
-        if (wo + 1024 * (d0 + d) < bytes)
-          __builtin_nontemporal_store(v[d], reinterpret_cast<u32x4*>(dst + wo + 1024 * (d0 + d)));
+        __builtin_amdgcn_raw_buffer_store_b128(v[d], w, wo + 1024 * (d0 + d), 0, kStoreAgentNT);
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -234,6 +238,12 @@ __device__ __forceinline__ uint32_t* step_counter(const FusedArgs& a, int lg, in
   return a.ctr + static_cast<int64_t>(a.LG) * a.n_strips + static_cast<int64_t>(lg) * a.S + h;
 }
 
+// Release at agent scope: write back this XCD's L2 so that the stores made
+// before it are visible to every XCD.  (A full __threadfence() would also
+// invalidate the L2, throwing away the operand lines every tile on the XCD
+// is reusing.)
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
 // Thread 0: the finished chunks of this workgroup are in L2 (every wave
 // waited for its stores and passed a barrier): count them, towards their
 // strip and their step (no atomic's return is waited for).
@@ -286,10 +296,12 @@ __device__ __forceinline__ void copy_claimed(const FusedArgs& a, int p0, int p1,
     const ChunkAt at = chunk_at(a, sh, p - sh.base);
     copy_piece(a, sh.piece, a.strip_list[at.pos], at.lg, at.piece, smem);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are in L2
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
   barrier_only();
   if (threadIdx.x == 0) {
-    __threadfence();  // write back the pieces, then count them
+    // pieces copied by the register loop (column strips, units under 16
+    // bytes) sit in L2: write them back before they are counted
+    if (a.unit != 16 || a.strided) release_agent();
     k = 0;
     for (int p = p0; p < p1; ++p) {
       while (p >= a.steps[a.claim_steps[k]].base + a.steps[a.claim_steps[k]].n_chunks) ++k;
@@ -462,7 +474,7 @@ fused_run_kernel(FusedArgs a) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           barrier_only();
           if (tid == 0) {
-            __threadfence();
+            release_agent();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
           }
           barrier_only();
@@ -518,15 +530,12 @@ fused_run_kernel(FusedArgs a) {
         if (lc.chunks == 0 && tid == 0) count_chunk(a, lp_step, lp_chunk);  // an empty piece
       }
     }
-    // the piece's stores have reached L2 in every wave: write them back and count the piece
+    // the piece's stores (agent-coherent) are complete in every wave: count the piece
     const auto after_loop = [&]() {
       if (lc.chunks > 0) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         barrier_only();
-        if (tid == 0) {
-          __threadfence();
-          count_chunk(a, lp_step, lp_chunk);
-        }
+        if (tid == 0) count_chunk(a, lp_step, lp_chunk);
       }
     };
     gemm_tile<IN, OUT, true>(gp, l, tm, tn, smem, &lc, after_loop);
@@ -553,9 +562,11 @@ fused_run_kernel(FusedArgs a) {
   }
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
-    __threadfence();
+    release_agent();
     const int old = __hip_atomic_fetch_add(nexit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bcast[4] = old == static_cast<int>(gridDim.x) - 1;
+    const bool last = old == static_cast<int>(gridDim.x) - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    bcast[4] = last;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier_only();
@@ -572,7 +583,7 @@ fused_run_kernel(FusedArgs a) {
     }
     if (a.times_next)
       for (int x = tid; x < 1 + 3 * a.S; x += kThreads) a.times_next[x] = 0;
-    __threadfence();
+    release_agent();
   }
 }
 

@@ -745,8 +745,10 @@ __device__ __forceinline__ void epilogue_staged(uint8_t* smem, int wave, int lan
 // the stores of slab kt retire before the wait of slab kt + 1 in the same
 // way.  A tile of KT slabs copies at most KT - 2 chunks; the descriptors
 // cover exactly the piece's bytes (a multiple of 16), so the last chunk's
-// lanes past its end neither read nor write.  Non-temporal: the bytes are
-// not reused by this tile.
+// lanes past its end neither read nor write.  Non-temporal (the bytes are
+// not reused by this tile), and the stores agent-coherent (sc1: written
+// through to where every XCD reads), so publishing the piece needs no L2
+// write-back.
 struct LoopCopy {
   const uint8_t* src;
   uint8_t* dst;
@@ -845,7 +847,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
         const uint32_t o = cvoff + static_cast<uint32_t>(ld_j - 1) * kLoopCopyChunk;
 #pragma unroll
         for (int op = 0; op < kLoopCopyOps; ++op)
-          __builtin_amdgcn_raw_buffer_store_b128(cb[op], cdst, o + op * 1024, 0, 2);
+          __builtin_amdgcn_raw_buffer_store_b128(cb[op], cdst, o + op * 1024, 0, 18);  // nt sc1
       }
       if (m == M::kCopyAt + M::kCopyEvery && loads && ld_j < n_chunks && kt_cur == ld_at) {
         const uint32_t o = cvoff + static_cast<uint32_t>(ld_j) * kLoopCopyChunk;
