@@ -605,7 +605,9 @@ int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, c
   // segments
   std::vector<std::pair<int, int>> segr;  // first and last step
   segr.push_back({0, 0});
-  for (int h = 1; h < S; h += o.max_group) segr.push_back({h, std::min(S - 1, h + o.max_group - 1)});
+  // step 1 alone: the launch's first round then waits for as little as it can
+  if (S > 1) segr.push_back({1, 1});
+  for (int h = 2; h < S; h += o.max_group) segr.push_back({h, std::min(S - 1, h + o.max_group - 1)});
   const int G = static_cast<int>(segr.size());
   std::vector<int> seg_of(S, 0);
   std::vector<dg::FusedSeg> segs(G);
@@ -631,9 +633,9 @@ int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, c
   // deadlines allow (the pieces of steps up to h are claimed by tiles that
   // start before step h's segment can: n_wg per round), down to 64 KiB.
   // Quota form (column strips, rows not 16-byte multiples, fewer than 6
-  // slabs, COPY_AHEAD 0, or no step after h1): list 1 is empty, pieces of
-  // about a quarter of the copy bytes per claimer (whole 32 KiB above that,
-  // at least 4 KiB, at most COPY_CHUNK bytes).
+  // slabs, or no step after h1): list 1 is empty, pieces of about a quarter
+  // of the copy bytes per claimer (whole 32 KiB above that, at least 4 KiB,
+  // at most COPY_CHUNK bytes).
   const int64_t per_q = std::max(1, o.n_wg / nq);  // the first round: the first per_q items of every queue
   auto items_of = [&](int g, int q) -> int64_t {
     return (segs[g].tiles / nq + (q < segs[g].tiles % nq ? 1 : 0)) * L;
@@ -659,8 +661,7 @@ int compute_fused(const Problem& pr, const std::vector<dist_gemm_step>& steps, c
   const int h1 = segr[g_first].second;
   const int64_t KT = (pr.K * pr.es_in + dg::kRowBytes - 1) / dg::kRowBytes;
   const int64_t cap = std::max<int64_t>(0, KT - 2) * dg::kLoopCopyBytes;
-  const bool loop = !sg.strided && sg.row_bytes % 16 == 0 && o.copy_ahead >= 1 && cap >= 4 * dg::kLoopCopyBytes &&
-                    h1 < S - 1;
+  const bool loop = !sg.strided && sg.row_bytes % 16 == 0 && cap >= 4 * dg::kLoopCopyBytes && h1 < S - 1;
   int64_t piece0, piece1;
   if (loop) {
     piece0 = std::min<int64_t>(sg.strip_bytes, 131072);

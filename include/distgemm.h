@@ -202,7 +202,9 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     element is computed exactly as by its own step.  The step that uses
  *     the local shard launches alone.  Mode 1: the tiles of g consecutive
  *     staged steps form one queue segment, ordered and split over the work
- *     queues together.  1 = one launch / segment per step; default 2.
+ *     queues together (step 1 always alone, so that the launch's first
+ *     round of tiles waits for as little as it can).  1 = one launch /
+ *     segment per step; default 2.
  *   DIST_GEMM_OPT_EXECUTION: how a run with more than one step executes.
  *     0 = step launches and side-stream copies (the options above apply);
  *     1 (default) = one persistent launch on the caller's stream does
@@ -239,21 +241,23 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     time.  Waits run out when the launch cannot keep a workgroup running
  *     on every work queue (other kernels holding the device's CUs), never
  *     in an unshared device; 0 makes every wait copy its own strip.
- *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 0..64; default 1.  With D >= 1
- *     and row strips (AG_ROT_A, AG_ROT_B, RS_TILE_A_ROT_C) whose rows are
- *     a multiple of 16 bytes, K of at least 6 slabs (over 640 bytes of a row of
- *     A) and steps left after those the launch's first round of tiles
- *     reads: the in-loop form.  Every tile that starts its GEMM while
- *     pieces of those later steps are left copies one inside its K loop
- *     (16 KiB per 128-byte K slab, loads and stores behind the slab's
- *     operand loads; a piece is an equal share of a strip no larger than
- *     the tile's K loop carries), and the tiles of the first round that
- *     wait copy the steps it reads.  Otherwise the quota form: every tile
- *     of the first D segments claims a quota of copy pieces before its
- *     GEMM (the staged pieces / (those tiles + the staged tiles of the
- *     launch's first round)), and waiting tiles copy the rest.  In both,
- *     workgroups with no tiles left copy whatever remains, and unaligned
- *     operand or image pointers send in-loop pieces to those too.
+ *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 0..64; default 1.  The staged
+ *     shards are copied in pieces from two lists: list 0, the steps the
+ *     launch's first round of tiles reads, and list 1, the later steps.
+ *     Every tile of the first D segments (default: the local step's, which
+ *     wait for nothing) claims a quota of list 0 before its GEMM (list 0 /
+ *     (those tiles + the staged tiles of the first round)); a tile whose
+ *     strip is not complete copies pieces while it waits.  For row strips
+ *     (AG_ROT_A, AG_ROT_B, RS_TILE_A_ROT_C) whose rows are a multiple of 16
+ *     bytes, with K of at least 6 slabs (over 640 bytes of a row of A) and
+ *     steps left after those the first round reads, list 1 is copied
+ *     inside K loops: every tile that starts its GEMM while pieces are left
+ *     copies one (16 KiB per 128-byte K slab, loads and stores behind the
+ *     slab's operand loads; pieces an equal share of a strip, no larger
+ *     than one K loop carries, as small as the steps' deadlines allow).
+ *     Otherwise list 0 holds every staged step.  Workgroups with no tiles
+ *     left copy whatever remains, and unaligned operand or image pointers
+ *     send in-loop pieces to them too.
  *   DIST_GEMM_OPT_SHARED_A: 1 = A holds one M x K matrix that every one of
  *     the L batches multiplies (B, C, D keep their L batches): the several-B
  *     form of the PyTorch symmetric-memory page's fused all-gather matmul
