@@ -171,6 +171,23 @@ def timed_runs(plan, args_run, steps, warmup, timing_runs, sampler=None, name="r
     return (t1 - t0) / steps * 1e3, step_ms, stats
 
 
+def flushed_runs(plan, args_run, steps, nbytes=1 << 30):
+    """Cold-cache timing: before each run a 1 GiB scratch buffer is written (the
+    last-level cache is 256 MB), and HIP events bracket the run alone."""
+    import torch
+    scratch = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (b, e) in enumerate(evs):
+        scratch.fill_(float(i))
+        b.record()
+        plan.run(*args_run)
+        e.record()
+    torch.cuda.synchronize()
+    ms = sorted(b.elapsed_time(e) for b, e in evs)
+    del scratch
+    return {"mean": sum(ms) / len(ms), "median": ms[len(ms) // 2], "min": ms[0]}
+
+
 def cpu_baseline(w, x, rows_per_block):
     """The oracle (as it stands) on a sample: rows_per_block rows from each of
     the S row blocks (or S x rows_per_block rows for column schedules), all N
@@ -395,6 +412,14 @@ def measure(w, args, headline):
     achieved_busy = w.flops / (busy * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/run, {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak); "
         f"{n_launch} launches/run, per-launch {achieved:.1f} TFLOP/s")
+    flushed = None
+    if args.flush:
+        plan.set_option("STEP_TIMING", 0)
+        fl = flushed_runs(plan, run_args, args.steps)
+        flushed = {"run_ms": {k: round(v, 4) for k, v in fl.items()},
+                   "tflops_mean": round(w.flops / (fl["mean"] * 1e-3) / 1e12, 2),
+                   "what": "1 GiB scratch written before each run (cold last-level cache); events around the run"}
+        log(f"[bench] flushed-cache runs: {flushed}")
     parity = parity_spot_check(w, x, D)
     log(f"[bench] parity spot check: {parity}")
     mono = None
@@ -448,6 +473,7 @@ def measure(w, args, headline):
         # copies it is the monolithic kernel: t_nocopy is its time
         "t_nocopy_ms": mono["ms"] if (mono and args.execution == 1) else None,
         "t_copy_only": copy_alone,
+        "flushed": flushed,
         "parity": parity,
         "device_wait_timeouts": wait_timeouts,
     }
@@ -457,7 +483,8 @@ def measure(w, args, headline):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # 100 timed runs per workload, the CUTLASS example page's default iteration count
+    ap.add_argument("--steps", type=int, default=100)
     # untimed runs before each timed set: the clock dips for the first tens of
     # runs of a sudden sustained load and recovers after about a hundred
     ap.add_argument("--warmup", type=int, default=100)
@@ -477,6 +504,8 @@ def main():
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-mono", action="store_true", help="skip the monolithic comparison")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time runs with a 1 GiB scratch write before each (cold caches), reported separately")
     ap.add_argument("--no-sub", action="store_true",
                     help="time only --config, not the other TP=8 workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -546,6 +575,7 @@ def main():
         "monolithic": rec["monolithic"],
         "t_nocopy_ms": rec["t_nocopy_ms"],
         "t_copy_only": rec["t_copy_only"],
+        "flushed": rec["flushed"],
         "parity": rec["parity"],
         "device_wait_timeouts": rec["device_wait_timeouts"],
         "cpu_baseline": cpu,
