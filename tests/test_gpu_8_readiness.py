@@ -240,3 +240,48 @@ def test_table_options_refused_after_capture():
             torch.cuda.synchronize()
             _ = (A.float() * 2).sum().item()
             assert torch.equal(D, ref), f"replay {i}"
+
+
+def _offset_like(t):
+    """t's values in a fresh buffer that starts one element past an aligned
+    address."""
+    import torch
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = flat[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("sched,dtype", [("AG_ROT_A", "BF16_F32"), ("AG_ROT_B", "BF16_BF16"),
+                                         ("RS_TILE_A_ROT_C", "BF16_F32")])
+def test_in_loop_copy_and_its_fallback(sched, dtype):
+    """Shapes whose later steps are copied inside K loops (8192 x 4096 x 1024
+    at TP=8: 16 slabs per tile, 512 tiles, so the first round of 256 reads
+    steps 0-3 only).  With the rotating operand one element past an aligned
+    address the in-loop copy is off and waiting and finished workgroups copy
+    those steps; both runs, with and without a copy delay, equal the
+    monolithic GEMM bit for bit, with no timed-out wait, and sampled outputs
+    match the oracle."""
+    import torch
+    from gpu_helpers import check_sampled, sample_indices
+    M, N = (8192, 4096) if sched != "AG_ROT_B" else (4096, 8192)
+    w = _case(sched, dtype, M, N, 1024, 1, 8, seed=131)
+    x = workloads.generate(w)
+    A, B, C = to_gpu(x.A), to_gpu(x.B), to_gpu(x.C)
+    ref = run_plan(w, x, schedule="MONOLITHIC", TP=1, dev=(A, B, C))
+    rot = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2}[sched]
+    for off in (False, True):
+        dev = [A, B, C]
+        if off:
+            dev[rot] = _offset_like(dev[rot])
+        for delay in (0, 2000):
+            log("case", w.name, "offset", off, "delay", delay)
+            with _plan(w, x, {"EXECUTION": 1, "COPY_DELAY_US": delay}) as p:
+                D = empty_out(w)
+                p.run(*_args(w, tuple(dev)), D, w.alpha, w.beta)
+                torch.cuda.synchronize()
+                assert p.device_errors() == 0
+            assert torch.equal(D, ref), (off, delay)
+    rows = sample_indices(M, 8, 2, seed=3)
+    cols = sample_indices(N, 8, 2, seed=4)
+    check_sampled(w, x, ref, rows, cols)
