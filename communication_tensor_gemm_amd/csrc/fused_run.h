@@ -40,41 +40,46 @@
 // pieces copied through LDS by every workgroup of the first round: the
 // tiles of the first segments (which read the local shard) claim a quota
 // before their GEMM, and a tile of a staged strip that is not yet complete
-// claims pieces one at a time while it waits (list 0, then list 1) instead
-// of spinning.  A tile that starts its GEMM claims one piece of list 1 and
-// copies it inside its K loop, where the copy's loads and stores ride in the
-// shadow of the MFMAs; list-1 pieces are sized so that the tiles starting
-// before a step's segment carry all of its pieces.  (Where a piece cannot be
-// copied inside the loop -- column strips, unaligned rows, too few slabs --
-// list 1 is empty and list 0 holds every staged step.)  Workgroups whose
-// queue is empty claim whatever is left.
+// claims pieces one at a time while it waits (list 0, then, for a strip of
+// list 1, list 1) instead of spinning.  A tile that starts its GEMM claims
+// one piece of list 1 and copies it inside its K loop, where the copy's
+// loads and stores ride in the shadow of the MFMAs; list-1 pieces are sized
+// so that the tiles starting before a step's segment carry all of its
+// pieces.  (Where a piece cannot be copied inside the loop -- column
+// strips, unaligned rows, too few slabs -- list 1 is empty and list 0 holds
+// every staged step.)  Workgroups whose queue is empty claim whatever is
+// left.
 //
 // Progress.  A workgroup copies what it claims before it waits on
 // anything (an in-loop piece is claimed only once the tile's own wait is
-// over), and a waiting workgroup claims while pieces are left; once none
-// are left, every piece is held by a running workgroup that finishes it
-// without waiting.  So every wait ends, given that every queue keeps at
-// least one running workgroup (the host orders single-launch runs on a
-// device one after another).  Should a wait nevertheless outlast its limit
-// (another kernel holding CUs, say), the workgroup copies its strip itself
-// -- the same bytes the claimers write, so the duplicate is harmless, and
-// the strip's region of G is read by no tile that has already finished --
-// counts the event, and goes on with a correct result.
+// over), and a workgroup waiting for a strip claims from the strip's list
+// while pieces are left; once none are left, every piece of that list is
+// held by a running workgroup that finishes it without waiting.  So every
+// wait ends, given that every queue keeps at least one running workgroup
+// (the host orders single-launch runs on a device one after another).
+// Should a wait nevertheless outlast its limit (another kernel holding CUs,
+// say), the workgroup copies its strip itself -- the same bytes the
+// claimers write, so the duplicate is harmless, and the strip's region of G
+// is read by no tile that has already finished -- counts the event, and
+// goes on with a correct result.
 //
-// Visibility.  Every wave of a claimer waits until its piece stores have
-// reached L2; after a barrier thread 0 releases at agent scope (L2
-// write-back only: no invalidate, which would cost every tile on the XCD
-// its cached operand lines) and adds the pieces to their strips' counters;
-// a waiting thread polls the counter with agent-scope loads and then
-// performs an agent-scope acquire (cache invalidate) before the barrier
-// that releases its workgroup into the tile.  Every piece also counts towards its step, so
-// to keep acquires rare thread 0 reads, after its strip, the step's count
-// once: when the whole step is complete (the usual case, the copies run
-// ahead), the acquire covers every strip of the step and later tiles of the
-// step wait no more; otherwise only the strip is remembered.  The counts
-// are added without waiting for the atomics' return.  All counters are
-// reset by the last workgroup to finish, so every launch starts from zero
-// (also when replayed from a graph).
+// Visibility.  The LDS copy and the in-loop copy store with agent scope
+// (written through to where every XCD reads); every wave of a claimer waits
+// until its stores are complete, and after a barrier thread 0 adds the
+// pieces to their strips' counters.  (The register copy loop, used for
+// column strips and units under 16 bytes, stores normally: thread 0 then
+// releases at agent scope first, an L2 write-back without the invalidate
+// that would cost every tile on the XCD its cached operand lines.)  A
+// waiting thread polls the counter with agent-scope loads and then performs
+// an agent-scope acquire (cache invalidate) before the barrier that releases
+// its workgroup into the tile.  Every piece also counts towards its step,
+// so to keep acquires rare thread 0 reads, after its strip, the step's
+// count once: when the whole step is complete (the usual case, the copies
+// run ahead), the acquire covers every strip of the step and later tiles of
+// the step wait no more; otherwise only the strip is remembered.  The
+// counts are added without waiting for the atomics' return.  All counters
+// are reset by the last workgroup to finish, so every launch starts from
+// zero (also when replayed from a graph).
 #pragma once
 #include "gemm_tile.h"
 
@@ -422,7 +427,9 @@ fused_run_kernel(FusedArgs a) {
               }
               if (pc + 1 >= a.list_end[0]) done0 = true;
             }
-            if (!ready && state == 0 && !done1) {
+            // list 1 only for a strip of list 1: a tile of the first round waits
+            // for list 0 alone, and a big in-loop piece would hold it back
+            if (!ready && state == 0 && !done1 && own.base >= a.list_begin[1]) {
               const int pc = a.list_begin[1] +
                              __hip_atomic_fetch_add(claim1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               if (pc < a.list_end[1]) {
