@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     Plan,
     dist_gemm_destroy,
     dist_gemm_device_errors,
+    dist_gemm_fused_tables,
     dist_gemm_plan,
     dist_gemm_plan_steps,
     dist_gemm_run,

@@ -26,7 +26,7 @@ ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "UNSUPPORTED", -4: "OOM", -5: "HIP"}
 
 # C functions declared in include/distgemm.h (checked by the CPU tests)
-C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_result_scale",
+C_FUNCTIONS = ("dist_gemm_step_table", "dist_gemm_fused_tables", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_result_scale",
                "dist_gemm_set_bias",
                "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_run_noalloc",
                "dist_gemm_plan_steps", "dist_gemm_step_times", "dist_gemm_step_timeline", "dist_gemm_device_errors",
@@ -49,6 +49,14 @@ class Step(ctypes.Structure):
                 self.n1)
 
 
+class FusedInfo(ctypes.Structure):
+    _fields_ = [("n_strips", ctypes.c_int32), ("n_segs", ctypes.c_int32), ("LG", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("strided", ctypes.c_int32), ("loop", ctypes.c_int32),
+                ("n_list0", ctypes.c_int32), ("n_list1", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("strip_bytes", ctypes.c_int64), ("ext", ctypes.c_int64),
+                ("row_bytes", ctypes.c_int64), ("height", ctypes.c_int64), ("loop_capacity", ctypes.c_int64)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -63,6 +71,8 @@ def _load() -> ctypes.CDLL:
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.dist_gemm_step_table.argtypes = [i64, i64, i64, i64, i32, i32, i32,
                                          ctypes.POINTER(Step), ctypes.POINTER(i32)]
+    lib.dist_gemm_fused_tables.argtypes = [i64, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, i64, i32,
+                                           ctypes.POINTER(FusedInfo), vp, vp, vp, vp]
     lib.dist_gemm_plan.argtypes = [i64, i64, i64, i64, i32, i32, i32, ctypes.POINTER(vp)]
     lib.dist_gemm_set_scales.argtypes = [vp, ctypes.c_float, ctypes.c_float]
     lib.dist_gemm_set_bias.argtypes = [vp, vp]
@@ -82,7 +92,7 @@ def _load() -> ctypes.CDLL:
     lib.dist_gemm_last_error.restype = ctypes.c_char_p
     lib.dist_gemm_status_string.argtypes = [i32]
     lib.dist_gemm_status_string.restype = ctypes.c_char_p
-    for name in ("dist_gemm_step_table", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_result_scale",
+    for name in ("dist_gemm_step_table", "dist_gemm_fused_tables", "dist_gemm_plan", "dist_gemm_set_scales", "dist_gemm_set_result_scale",
                  "dist_gemm_set_bias",
                  "dist_gemm_set_option", "dist_gemm_run", "dist_gemm_run_ag", "dist_gemm_run_noalloc",
                  "dist_gemm_plan_steps",
@@ -113,6 +123,30 @@ def dist_gemm_step_table(M, N, K, L, TP, schedule, dtype) -> List[tuple]:
     _check(lib.dist_gemm_step_table(M, N, K, L, TP, _enum(SCHEDULES, schedule),
                                     _enum(DTYPES, dtype), arr, ctypes.byref(n)))
     return [s.as_tuple() for s in arr]
+
+
+def dist_gemm_fused_tables(M, N, K, L, TP, schedule, dtype, shared_a=0, queues=8, step_group=2, copy_ahead=1,
+                           copy_chunk=2 << 20, n_wg=256) -> dict:
+    """The single launch's tables for these options (host only): the info
+    fields, and the arrays segs [n_segs][4], steps [TP][7], strips
+    [2 n_strips + TP], seg [queues][n_segs + 1] as lists of rows."""
+    info = FusedInfo()
+    args = (M, N, K, L, TP, _enum(SCHEDULES, schedule), _enum(DTYPES, dtype), shared_a, queues, step_group,
+            copy_ahead, copy_chunk, n_wg)
+    _check(lib.dist_gemm_fused_tables(*args, ctypes.byref(info), None, None, None, None))
+    segs = (ctypes.c_int32 * (4 * info.n_segs))()
+    steps = (ctypes.c_int64 * (7 * TP))()
+    strips = (ctypes.c_int32 * (2 * info.n_strips + TP))()
+    seg = (ctypes.c_int32 * (queues * (info.n_segs + 1)))()
+    _check(lib.dist_gemm_fused_tables(*args, ctypes.byref(info), segs, steps, strips, seg))
+    out = {name: getattr(info, name) for name, _ in FusedInfo._fields_ if name != "reserved"}
+    out["segs"] = [list(segs[4 * g:4 * g + 4]) for g in range(info.n_segs)]
+    out["steps"] = [list(steps[7 * h:7 * h + 7]) for h in range(TP)]
+    out["strip_list"] = list(strips[:info.n_strips])
+    out["strip_step"] = list(strips[info.n_strips:2 * info.n_strips])
+    out["claim_steps"] = list(strips[2 * info.n_strips:])
+    out["seg"] = [list(seg[q * (info.n_segs + 1):(q + 1) * (info.n_segs + 1)]) for q in range(queues)]
+    return out
 
 
 def dist_gemm_plan(M, N, K, L, TP, schedule, dtype) -> ctypes.c_void_p:

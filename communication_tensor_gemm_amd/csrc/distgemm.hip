@@ -1064,6 +1064,75 @@ int dist_gemm_step_table(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int
   return DIST_GEMM_OK;
 }
 
+int dist_gemm_fused_tables(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+                           int shared_a, int queues, int step_group, int copy_ahead, int64_t copy_chunk,
+                           int n_wg, dist_gemm_fused_info* info, int32_t* segs, int64_t* steps,
+                           int32_t* strips, int32_t* seg) {
+  if (!info) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "info is NULL");
+  Problem pr;
+  const int rc = validate(M, N, K, L, TP, schedule, dtype, &pr, nullptr);
+  if (rc != DIST_GEMM_OK) return rc;
+  if (shared_a != 0 && shared_a != 1) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "shared A must be 0 or 1");
+  if (queues != 1 && queues != dg::kMaxQueues) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "queues must be 1 or 8");
+  if (step_group < 1 || step_group > 1024) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "step group must be 1..1024");
+  if (copy_ahead < 0 || copy_ahead > 64) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "copy-ahead segments must be 0..64");
+  if (copy_chunk < 4096 || copy_chunk > (int64_t{1} << 28) || copy_chunk % 16 != 0)
+    return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "copy chunk must be a multiple of 16 in [4096, 2^28]");
+  if (n_wg < queues || n_wg % queues != 0)
+    return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "workgroups must be a positive multiple of the queues");
+  if (pr.S < 2 || pr.schedule == DIST_GEMM_MONOLITHIC)
+    return fail(nullptr, DIST_GEMM_ERR_UNSUPPORTED, "the single launch needs at least two steps");
+  pr.shared_a = shared_a != 0;
+  FusedOpts o;
+  o.queues = queues;
+  o.copy_chunk = copy_chunk;
+  o.copy_ahead = copy_ahead;
+  o.max_group = step_group;
+  o.n_wg = n_wg;
+  FusedTables t;
+  std::string err;
+  const int rc2 = compute_fused(pr, build_steps(pr), o, &t, &err);
+  if (rc2 != DIST_GEMM_OK) {
+    g_last_error = err;
+    return rc2;
+  }
+  const StripGeom sg = strip_geom(pr);
+  const int S = pr.S;
+  const int n_strips = static_cast<int>((sg.ext + dg::kBM - 1) / dg::kBM);
+  const int G = static_cast<int>(t.segs.size());
+  info->n_strips = n_strips;
+  info->n_segs = G;
+  info->LG = sg.LG;
+  info->cols = sg.cols;
+  info->strided = sg.strided;
+  info->loop = t.loop ? 1 : 0;
+  info->n_list0 = t.n_list0;
+  info->n_list1 = t.n_list1;
+  info->n_local = t.n_local;
+  info->strip_bytes = sg.strip_bytes;
+  info->ext = sg.ext;
+  info->row_bytes = sg.row_bytes;
+  info->height = sg.height;
+  const int64_t KT = (pr.K * pr.es_in + dg::kRowBytes - 1) / dg::kRowBytes;
+  info->loop_capacity = std::max<int64_t>(0, KT - 2) * dg::kLoopCopyBytes;
+  if (segs)
+    for (int g = 0; g < G; ++g) {
+      segs[4 * g + 0] = t.segs[g].strip0;
+      segs[4 * g + 1] = t.segs[g].nst;
+      segs[4 * g + 2] = t.segs[g].tiles;
+      segs[4 * g + 3] = t.segs[g].quota;
+    }
+  if (steps)
+    for (int h = 0; h < S; ++h) {
+      const dg::FusedStepCopy& c = t.copies[h];
+      int64_t* r = steps + 7 * h;
+      r[0] = c.piece; r[1] = c.strip0; r[2] = c.nst; r[3] = c.P; r[4] = c.n_chunks; r[5] = c.wait; r[6] = c.base;
+    }
+  if (strips) std::copy(t.strips.begin(), t.strips.end(), strips);
+  if (seg) std::copy(t.seg.begin(), t.seg.end(), seg);
+  return DIST_GEMM_OK;
+}
+
 int dist_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
                    dist_gemm_plan_t* out) {
   if (!out) return fail(nullptr, DIST_GEMM_ERR_INVALID_ARG, "out is NULL");

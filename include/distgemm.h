@@ -129,6 +129,50 @@ typedef struct dist_gemm_step {
 int dist_gemm_step_table(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule,
                          int dtype, dist_gemm_step* out, int* n_steps);
 
+/* The single launch's work and copy tables (dist_gemm_run's default
+ * execution), computed on the host with no device work, for checking the
+ * schedule's bookkeeping on a CPU: exactly the tables a plan with these
+ * options builds for a device running n_wg workgroups (the plan uses one
+ * per CU, rounded down to a multiple of the queues).  Validates the
+ * problem as dist_gemm_step_table does and the options as
+ * dist_gemm_set_option does (SHARED_A, QUEUES, STEP_GROUP, COPY_AHEAD,
+ * COPY_CHUNK); UNSUPPORTED for MONOLITHIC or one step.  `info` is
+ * required; each array may be NULL (call once with NULLs to size them):
+ *   segs   [n_segs][4]: first strip-list position, strips, tiles per batch,
+ *          quota (list-0 pieces each tile claims before its GEMM);
+ *   steps  [TP][7]: piece size (bytes; column strips: rows), first
+ *          strip-list position, strips, pieces per strip (a strip's counter
+ *          target per batch), pieces (strips x batches x pieces per strip),
+ *          1 if its tiles wait for their strip, first piece in claim order;
+ *   strips [2 n_strips + TP]: the strip list (step by step), the step of
+ *          each position, the steps in claim order (1 .. TP-1, then 0);
+ *   seg    [queues][n_segs + 1]: the first item of each segment in each
+ *          queue (items of a queue: its share of each segment's tile order,
+ *          batch by batch), then the queue's item count.
+ * Claim lists (the gathered image not returned): list 0 is pieces
+ * [0, n_list0) of the claim order, list 1 [n_list0, n_list0 + n_list1);
+ * step 0's n_local pieces follow and join the last nonempty list when the
+ * gathered image is returned. */
+typedef struct dist_gemm_fused_info {
+  int32_t n_strips;       /* strips (256 rows or columns) per batch of the gathered operand */
+  int32_t n_segs;         /* queue segments */
+  int32_t LG;             /* batches of the gathered image */
+  int32_t cols;           /* 1: a strip is a tile column, else a tile row */
+  int32_t strided;        /* 1: a strip is 256 columns of every row (RS_TILE_B_ROT_C) */
+  int32_t loop;           /* 1: list 1 is copied inside K loops, one piece per starting tile */
+  int32_t n_list0, n_list1, n_local;
+  int32_t reserved;
+  int64_t strip_bytes;    /* bytes of a full strip of one batch */
+  int64_t ext;            /* rows (row strips) or columns (column strips) of the operand */
+  int64_t row_bytes;      /* row strips: bytes per row; column strips: element bytes */
+  int64_t height;         /* column strips: rows per batch */
+  int64_t loop_capacity;  /* bytes one tile's K loop copies at most */
+} dist_gemm_fused_info;
+int dist_gemm_fused_tables(int64_t M, int64_t N, int64_t K, int64_t L, int TP, int schedule, int dtype,
+                           int shared_a, int queues, int step_group, int copy_ahead, int64_t copy_chunk,
+                           int n_wg, dist_gemm_fused_info* info, int32_t* segs, int64_t* steps,
+                           int32_t* strips, int32_t* seg);
+
 /* Create a plan on the current HIP device: validates the problem (same
  * rules as dist_gemm_step_table), builds the step table, allocates the
  * gathered image of the rotating operand (A for AG_ROT_A, B for AG_ROT_B,
