@@ -845,8 +845,7 @@ dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, c
   a.nq = queues;
   a.S = pr.S;
   a.copy_on = copy_on ? 1 : 0;
-  a.copy_local = copy_local ? 1 : 0;
-  // step 0's pieces (copy_local) close the last list in use
+  // step 0's pieces (copied when G is returned) close the last list in use
   const int nz = copy_local ? dv.n_local : 0;
   if (!copy_on) {
     a.list_begin[0] = a.list_end[0] = a.list_begin[1] = a.list_end[1] = 0;

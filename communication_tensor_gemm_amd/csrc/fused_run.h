@@ -263,19 +263,6 @@ __device__ __forceinline__ void count_chunk(const FusedArgs& a, int h, int c) {
     __hip_atomic_fetch_max(a.times + 1 + 3 * h, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Rank of item i of queue q among all items of a segment (T2 tiles per
-// batch, L batches, nq queues) in the order they start: by position in their
-// queue first, then by queue.  Queue q' holds n(q') = (T2/nq + (q' < T2 mod
-// nq)) * L items, so the rank is the number of items (i', q') with i' < i,
-// plus the queues before q that still have an item at position i.
-__device__ __forceinline__ int64_t item_rank(int i, int q, int T2, int L, int nq) {
-  const int qq = T2 / nq, r = T2 - qq * nq;
-  const int nA = (qq + 1) * L, nB = qq * L;
-  const int64_t before = static_cast<int64_t>(r) * min(i, nA) + static_cast<int64_t>(nq - r) * min(i, nB);
-  const int same = (nA > i ? min(q, r) : 0) + (nB > i ? max(0, q - r) : 0);
-  return before + same;
-}
-
 // The step whose pieces [base, base + n_chunks) of the claim order hold
 // piece p (claim_steps lists the steps in that order).
 __device__ __forceinline__ int piece_step(const FusedArgs& a, int p) {
@@ -285,7 +272,8 @@ __device__ __forceinline__ int piece_step(const FusedArgs& a, int p) {
 }
 
 // Copy pieces [p0, p1) of the claim order with the whole workgroup, then
-// (thread 0) write them back and count them.  The first copy of a workgroup waits for the delay test hook.
+// (thread 0) count them.  The first copy of a workgroup waits for the delay
+// test hook.
 __device__ __forceinline__ void copy_claimed(const FusedArgs& a, int p0, int p1, uint8_t* smem,
                                              bool& delayed, uint64_t t_start) {
   if (!delayed) {
@@ -362,7 +350,6 @@ fused_run_kernel(FusedArgs a) {
     const int qq = T2 / a.nq, r = T2 - qq * a.nq;
     const int share = qq + (q < r ? 1 : 0), first = q * qq + min(q, r);
     const int l = i / share, j = i - l * share;
-    const int gtiles = T2 * a.g.L;
     // the segment's tile order: groups of four tile rows walked column by
     // column, as the monolithic kernel walks (row strips: the rows are the
     // strips; column strips: the strips are the columns)

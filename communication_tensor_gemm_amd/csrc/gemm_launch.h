@@ -131,9 +131,8 @@ struct FusedArgs {
   int32_t unit;                  // copy unit: 16, 4 or 1 bytes
   int32_t n_seg, nq, S;
   int32_t copy_on;               // 0: nothing rotates (a reduce-scatter with beta = 0)
-  int32_t copy_local;            // 1: step 0's strips are copied into G too (G is returned)
   int32_t list_begin[2];         // claim lists this run: pieces [begin, end) of the claim order
-  int32_t list_end[2];           // (step 0's pieces at the end of the last list when copy_local)
+  int32_t list_end[2];           // (step 0's pieces close the last list when G is returned)
   int32_t loop_copy;             // 1: starting tiles copy a list-1 piece in their K loop
 };
 
