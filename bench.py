@@ -321,7 +321,7 @@ def make_plan(w, x, args, options=None):
     opts = {"COMPUTE_STREAMS": args.compute_streams, "COPY_ENGINE": args.copy_engine,
             "COPY_STREAMS": args.copy_streams, "STEP_GROUP": args.step_group,
             "EXECUTION": args.execution, "QUEUES": args.queues, "COPY_CHUNK": args.copy_chunk,
-            "COPY_AHEAD": args.copy_ahead}
+            "COPY_AHEAD": args.copy_ahead, "HALF_TILES": args.half_tiles}
     opts.update(options or {})
     for k, v in opts.items():
         plan.set_option(k, v)
@@ -428,6 +428,7 @@ def measure(w, args, headline):
         with dg.Plan(w.M, w.N, w.K, w.L, 1, "MONOLITHIC", w.dtype) as mp:
             if w.in_dtype == "e4m3":
                 mp.set_scales(x.scale_a, x.scale_b)
+            mp.set_option("HALF_TILES", args.half_tiles)
             mono_ms, mono_steps, mono_stats = timed_runs(mp, run_args, args.steps, args.warmup, True,
                                                          name=w.name + ".monolithic")
         mono = {"ms": round(mono_ms, 4), "tflops": round(w.flops / (mono_ms * 1e-3) / 1e12, 2),
@@ -500,6 +501,8 @@ def main():
     ap.add_argument("--copy-chunk", type=int, default=2 << 20, help="bytes per copy item of the single launch")
     ap.add_argument("--copy-ahead", type=int, default=1,
                     help="segments of the single launch whose tiles claim a copy quota before their GEMM")
+    ap.add_argument("--half-tiles", type=int, default=1,
+                    help="1: a last round of tiles that fills at most half the CUs runs as half-height tiles")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
@@ -548,7 +551,7 @@ def main():
                    "copy_streams": args.copy_streams, "step_group": args.step_group,
                    "execution": ["step_launches", "single_launch"][args.execution],
                    "queues": args.queues, "copy_chunk": args.copy_chunk,
-                   "copy_ahead": args.copy_ahead})
+                   "copy_ahead": args.copy_ahead, "half_tiles": args.half_tiles})
     out = {
         "metric": METRIC,
         "value": rec["value"],

@@ -19,7 +19,8 @@ SCHEDULES = {"AG_ROT_A": 0, "AG_ROT_B": 1, "RS_TILE_A_ROT_C": 2, "RS_TILE_B_ROT_
 DTYPES = {"F32": 0, "BF16_F32": 1, "BF16_BF16": 2, "E4M3_BF16": 3, "E4M3_F32": 4, "E4M3_E4M3": 5}
 OPTIONS = {"COMPUTE_STREAMS": 0, "COPY_ENGINE": 1, "STEP_TIMING": 2, "COPY_STREAMS": 3,
            "STEP_GROUP": 4, "EXECUTION": 5, "QUEUES": 6, "COPY_CHUNK": 7, "WAIT_LIMIT_US": 8,
-           "COPY_AHEAD": 9, "SHARED_A": 10, "COPY_DELAY_US": 11, "FAST_ACCUM": 12}
+           "COPY_AHEAD": 9, "SHARED_A": 10, "COPY_DELAY_US": 11, "FAST_ACCUM": 12,
+           "HALF_TILES": 13}
 # bytes per element of (A/B, C/D) for each dtype
 ELEM_BYTES = {"F32": (4, 4), "BF16_F32": (2, 4), "BF16_BF16": (2, 2), "E4M3_BF16": (1, 2),
               "E4M3_F32": (1, 4), "E4M3_E4M3": (1, 1)}

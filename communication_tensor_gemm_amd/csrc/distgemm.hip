@@ -232,6 +232,7 @@ struct dist_gemm_plan_s {
   float scale_a = 1.0f, scale_b = 1.0f;
   float result_scale = 1.0f;   // e4m3 output only
   int fast_accum = 0;          // accepted; gfx950 MFMAs accumulate in fp32 either way
+  int half_tiles = 1;          // a last partial round of tiles runs as half-height tiles
   const void* bias = nullptr;  // device, N values of the output type, or NULL
   int compute_streams = 2;
   int copy_engine = 2;  // library streaming copy kernel
@@ -455,6 +456,7 @@ dg::GemmParams step_params(const dist_gemm_plan_s* P, const dist_gemm_step& st, 
   g.alpha = alpha;
   g.beta = beta;
   g.post = P->result_scale;
+  g.tail_cus = P->half_tiles ? P->n_cu / dg::kNumXcd : 0;
   g.M = y.M;
   g.N = y.N;
   g.A = (y.stagedA ? stg : static_cast<const uint8_t*>(A)) + y.offA;
@@ -862,6 +864,7 @@ dg::FusedArgs fused_args(const Problem& pr, const FusedDevice& dv, int queues, c
   // the in-loop copy moves whole 16-byte units (else the list-1 pieces go to
   // waiting and finished workgroups)
   a.loop_copy = copy_on && dv.loop && dv.n_list1 > 0 && a.unit == 16 ? 1 : 0;
+  a.half_tail = 1;
   return a;
 }
 
@@ -905,6 +908,7 @@ int run_fused(dist_gemm_plan_s* P, hipStream_t st, const void* A, const void* B,
                                P->copy_delay_us * P->clock_khz / 1000);
   a.times = times;
   a.times_next = times_next;
+  a.half_tail = P->half_tiles;
   const int grid = std::max(P->queues, P->n_cu / P->queues * P->queues);
   return launch_ordered(P->device, pr.in_kind, pr.out_kind, a, grid, st, &P->err, [] { return DIST_GEMM_OK; });
 }
@@ -1304,6 +1308,11 @@ int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value) {
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "fast accumulate must be 0 or 1");
       plan->fast_accum = static_cast<int>(value);
       return DIST_GEMM_OK;
+    case DIST_GEMM_OPT_HALF_TILES:
+      if (value != 0 && value != 1)
+        return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "half tiles must be 0 or 1");
+      plan->half_tiles = static_cast<int>(value);
+      return DIST_GEMM_OK;
     case DIST_GEMM_OPT_COPY_DELAY_US:
       if (value < 0 || value > 1000000)
         return fail(&plan->err, DIST_GEMM_ERR_INVALID_ARG, "copy delay must be in [0, 1e6] us");
@@ -1655,6 +1664,7 @@ int dist_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t L, int TP, in
     g.M = static_cast<int32_t>(pr.M); g.N = static_cast<int32_t>(pr.N);
     g.K = static_cast<int32_t>(pr.K); g.L = static_cast<int32_t>(pr.L);
     g.alpha = alpha_eff; g.beta = beta; g.post = 1.0f;
+    g.tail_cus = nd.n_cu / dg::kNumXcd;
     DG_HIP(nullptr, dg::launch_gemm(pr.in_kind, pr.out_kind, g, st));
     return DIST_GEMM_OK;
   }

@@ -320,7 +320,12 @@ fused_run_kernel(FusedArgs a) {
   int32_t* const claim0 = a.sync + kSyncClaim * kSyncStride;
   int32_t* const claim1 = a.sync + (kSyncClaim + 1) * kSyncStride;
   const int32_t* const seg = a.seg + q * (a.n_seg + 1);
-  const int n_items = seg[a.n_seg];
+  // the queue's items: its tiles, except that the tiles of a last round
+  // that fills at most half of the queue's workgroups come as two
+  // half-height items each (consecutive, so a tile's halves wait alike)
+  const int n_tiles = seg[a.n_seg];
+  const int split = a.half_tail ? half_tail_tiles(n_tiles, static_cast<int>(gridDim.x) / a.nq) : 0;
+  const int whole = n_tiles - split, n_items = n_tiles + split;
   const uint64_t t_start = wall_clock64();
   if (a.times && tid == 0)
     __hip_atomic_fetch_max(a.times, ~t_start, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -340,8 +345,10 @@ fused_run_kernel(FusedArgs a) {
     if (tid == 0) bcast[0] = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_only();
-    const int k = __builtin_amdgcn_readfirstlane(bcast[0]);
-    if (k >= n_items) break;
+    const int item = __builtin_amdgcn_readfirstlane(bcast[0]);
+    if (item >= n_items) break;
+    const int k = item < whole ? item : whole + (item - whole) / 2;  // the queue's tile
+    const int hrow = item < whole ? -1 : (item - whole) & 1;           // half of a half-height item
     while (k >= seg[g + 1]) ++g;
     const FusedSeg& sg = a.segs[g];
     // the tile: position i of this queue's share of segment g
@@ -532,7 +539,10 @@ fused_run_kernel(FusedArgs a) {
         if (tid == 0) count_chunk(a, lp_step, lp_chunk);
       }
     };
-    gemm_tile<IN, OUT, true>(gp, l, tm, tn, smem, &lc, after_loop);
+    if (hrow < 0)
+      gemm_tile<IN, OUT, true>(gp, l, tm, tn, smem, &lc, after_loop);
+    else
+      gemm_tile<IN, OUT, true, true>(gp, l, tm, tn, smem, &lc, after_loop, hrow);
     if (a.times && tid == 0)
       __hip_atomic_fetch_max(a.times + 3 + 3 * h_own, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -25,12 +25,27 @@ struct GemmParams {
   int32_t M, N, K, L;
   float alpha, beta;
   float post;  // e4m3 output: the result scale, applied before the cast
+  // 0: whole tiles only.  Otherwise the CUs of one XCD: the workgroups of an
+  // XCD's last round of tiles, when that round fills at most half of them,
+  // each compute half a tile (128 x 256), so the round takes about half as
+  // long (L = 1 only).
+  int32_t tail_cus;
 };
+
+// Tiles of a last partial round that run as two half-height tiles each:
+// n tiles over `slots` concurrent workgroups.
+__host__ __device__ inline int half_tail_tiles(int n, int slots) {
+  if (slots <= 0) return 0;
+  const int rem = n % slots;
+  return (rem > 0 && 2 * rem <= slots) ? rem : 0;
+}
 
 // Macro tile of one workgroup, and the bytes of one operand row per K tile.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kRowBytes = 128;
+// XCDs of the chip: workgroup b of a launch runs on XCD b mod 8.
+constexpr int kNumXcd = 8;
 // Bytes a workgroup of the persistent kernel copies per K slab inside its K
 // loop (four waves, four 1 KiB loads each); a tile of KT slabs copies at
 // most KT - 2 such chunks.
@@ -134,6 +149,8 @@ struct FusedArgs {
   int32_t list_begin[2];         // claim lists this run: pieces [begin, end) of the claim order
   int32_t list_end[2];           // (step 0's pieces close the last list when G is returned)
   int32_t loop_copy;             // 1: starting tiles copy a list-1 piece in their K loop
+  int32_t half_tail;             // 1: a queue's last partial round of tiles, when it fills at
+                                 // most half of the queue's workgroups, runs as half-height tiles
 };
 
 // Enqueue the single-launch run on `stream` with `grid` workgroups (a

@@ -50,6 +50,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <algorithm>
+#include <type_traits>
 
 #include "gemm_launch.h"
 
@@ -79,7 +81,6 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // stay resident in the last-level cache together (measured: 4 beats 2, 6, 8,
 // 16 and 32 at 4096-16384 rows).
 constexpr int kGroupM = 4;
-constexpr int kNumXcd = 8;
 
 static_assert(kBM == 256 && kBN == 256, "tile geometry");
 static_assert(kRowBytes == kSlab, "slab width");
@@ -220,6 +221,8 @@ struct Mma;
 // lane%16 of the wave's 128 rows and chunk lane/16 of the half slab.
 struct Mma16Base {
   static constexpr int BLK = 16, NB = 8, R = 4;
+  static constexpr int NBM = NB;  // block rows of the wave's accumulator
+  static constexpr int kLoadsA = kLoadsPerOperand, kLoadsB = kLoadsPerOperand;  // DMA loads per wave per slab
   static constexpr int kReads = 16;
   typedef f32x4 Acc;
   typedef i32x4 Frags[16];  // 0..7: A blocks, 8..15: B blocks
@@ -284,6 +287,8 @@ struct Mma<IN_F32> : Mma16Base {
 // block, read as two 16-byte halves.
 struct Mma32Base {
   static constexpr int BLK = 32, NB = 4, R = 16;
+  static constexpr int NBM = NB;
+  static constexpr int kLoadsA = kLoadsPerOperand, kLoadsB = kLoadsPerOperand;
   static constexpr int kReads = 16;
   typedef f32x16 Acc;
   typedef i32x8 Frags[8];  // 0..3: A blocks, 4..7: B blocks (32 bytes per lane)
@@ -326,6 +331,95 @@ struct Mma<IN_E4M3> : Mma32Base {
   }
 };
 
+// Half-height tile (128 x 256, for the last round of tiles when it would
+// leave most CUs idle): each wave's accumulator is NBM = NB / 2 block rows
+// by NB block columns (64 x 128), A slabs hold 128 rows (4 DMA loads per
+// wave instead of 8), and a half slab takes half the MFMAs and NBM + NB
+// fragment reads (the NBM A blocks, then the other B blocks).  Every output
+// element is computed by the same MFMA instruction in the same K order as
+// in a full tile, so results are bitwise the same.
+template <int IN>
+struct MmaHalf;
+
+template <>
+struct MmaHalf<IN_BF16> : Mma16Base {
+  static constexpr int NBM = 4;
+  static constexpr int kLoadsA = 4;
+  static constexpr int kMfma = 32, kReads = 12;
+  static constexpr int kReadAt = 0, kReadEvery = 2, kReadsPer = 1;
+  static constexpr int kDmaAt = 1, kDmaEvery = 3;
+  static constexpr int kCopyAt = 25, kCopyEvery = 3;
+  // read q < 8: A block q/2 (q even) or B block q/2; q >= 8: B block q - 4
+  __device__ __forceinline__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+                                              Frags& F) {
+    if (q < 2 * NBM)
+      Mma16Base::read(q, a, b, fb, F);
+    else
+      F[8 + q - NBM] = *reinterpret_cast<const i32x4*>(b + fb[2] + kReadStride * (q - NBM));
+  }
+  __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NBM][NB]) {
+    const int i = m >> 3, j = m & 7;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc[i][j])
+                 : "v"(F[i]), "v"(F[8 + j]));
+  }
+};
+
+template <>
+struct MmaHalf<IN_F32> : Mma16Base {
+  static constexpr int NBM = 4;
+  static constexpr int kLoadsA = 4;
+  static constexpr int kMfma = 128, kReads = 12;
+  static constexpr int kReadAt = 1, kReadEvery = 4, kReadsPer = 1;
+  static constexpr int kDmaAt = 2, kDmaEvery = 8;
+  static constexpr int kCopyAt = 96, kCopyEvery = 16;
+  __device__ __forceinline__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+                                              Frags& F) {
+    if (q < 2 * NBM)
+      Mma16Base::read(q, a, b, fb, F);
+    else
+      F[8 + q - NBM] = *reinterpret_cast<const i32x4*>(b + fb[2] + kReadStride * (q - NBM));
+  }
+  // MFMA m: K step t = m / 32 of block ((m / 8) % 4, m % 8)
+  __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NBM][NB]) {
+    const int t = m >> 5, i = (m >> 3) & 3, j = m & 7;
+    const float a = __builtin_bit_cast(f32x4, F[i])[t];
+    const float b = __builtin_bit_cast(f32x4, F[8 + j])[t];
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(a), "v"(b));
+  }
+};
+
+template <>
+struct MmaHalf<IN_E4M3> : Mma32Base {
+  static constexpr int NBM = 2;
+  static constexpr int kLoadsA = 4;
+  static constexpr int kMfma = 8, kReads = 12;
+  static constexpr int kReadAt = 0, kReadEvery = 1, kReadsPer = 2;
+  static constexpr int kDmaAt = 0, kDmaEvery = 1;
+  static constexpr int kCopyAt = 6, kCopyEvery = 1;
+  // read q < 8: as the full tile's (blocks 0, 1 of A and B); q >= 8: B
+  // blocks 2, 3, half q % 2
+  __device__ __forceinline__ static void read(int q, const uint8_t* a, const uint8_t* b, const int (&fb)[4],
+                                              Frags& F) {
+    if (q < 8) {
+      Mma32Base::read(q, a, b, fb, F);
+    } else {
+      const int blk = 2 + ((q - 8) >> 1), h = q & 1;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(b + fb[2 + h] + kReadStride * blk);
+      if (h == 0)
+        F[4 + blk].lo = v;
+      else
+        F[4 + blk].hi = v;
+    }
+  }
+  __device__ __forceinline__ static void mma(int m, const Frags& F, Acc (&acc)[NBM][NB]) {
+    const int i = m >> 2, j = m & 3;
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                 : "+a"(acc[i][j])
+                 : "v"(F[i]), "v"(F[NB + j]));
+  }
+};
+
 // Tile-invariant addressing of one workgroup.
 //
 // LDS layout of one operand slab: 32 blocks of 8 rows x 128 bytes, block b
@@ -342,7 +436,7 @@ struct TileCtx {
   uint32_t lda16, ldb16;      // 16 rows of A / B in bytes (block pair stride)
   uint32_t gk[2];             // lane's K byte offset within a slab, even / odd blocks
   int kbytes;
-  int fill;                   // wave's first LDS block within an operand slab
+  int fillA, fillB;           // wave's first LDS block within an A / B slab (bytes)
 };
 
 __device__ __forceinline__ int slot_add(int s, int d) {
@@ -362,10 +456,13 @@ struct SlabLoad {
 #pragma unroll
     for (int odd = 0; odd < 2; ++odd)
       kinv[odd] = (static_cast<int>(k0b + c.gk[odd]) < c.kbytes) ? 0u : kOutOfRange;
-    r = OP == 0 ? make_rsrc(c.Ab + k0b, c.a_bytes - k0b) : make_rsrc(c.Bb + k0b, c.b_bytes - k0b);
-    dst = smem + slot * kOperandSlab + c.fill;
+    // bytes left from k0b (none: a half-height tile whose rows all lie past
+    // M has a_bytes = 0, and every load must then be out of range)
+    const uint32_t have = OP == 0 ? c.a_bytes : c.b_bytes;
+    r = make_rsrc((OP == 0 ? c.Ab : c.Bb) + k0b, have > k0b ? have - k0b : 0u);
+    dst = smem + slot * kOperandSlab + (OP == 0 ? c.fillA : c.fillB);
   }
-  // load d of the wave's eight: LDS block fill/1K + d, rows 8d.. of the wave's 64
+  // load d of the wave's: LDS block fill/1K + d, rows 8d.. of the wave's rows
   __device__ __forceinline__ void issue(const TileCtx& c, int d) const {
     const uint32_t* g = OP == 0 ? c.ga : c.gb;
     const uint32_t ld16 = OP == 0 ? c.lda16 : c.ldb16;
@@ -374,31 +471,30 @@ struct SlabLoad {
   }
 };
 
-template <int OP>
+template <typename M, int OP>
 __device__ __forceinline__ void issue_operand(const TileCtx& c, uint8_t* smem, int kt, int slot) {
   const SlabLoad<OP> L(c, smem, kt, slot);
 #pragma unroll
-  for (int d = 0; d < kLoadsPerOperand; ++d) L.issue(c, d);
+  for (int d = 0; d < (OP == 0 ? M::kLoadsA : M::kLoadsB); ++d) L.issue(c, d);
 }
 
 // One half slab: the MFMAs on Fm, with (kRead) the reads of the next half
 // slab into Fr from LDS bases ra / rb and (kIssue) the DMA of operand kOp of
 // slab kt_issue into ring slot slot_issue, in the type's fixed order.
-template <int IN, bool kIssue, bool kRead, int kOp, typename X>
+template <typename M, bool kIssue, bool kRead, int kOp, typename X>
 __device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int kt_issue,
                                           int slot_issue, const uint8_t* ra, const uint8_t* rb,
-                                          const int (&fb)[4], const typename Mma<IN>::Frags& Fm,
-                                          typename Mma<IN>::Frags& Fr,
-                                          typename Mma<IN>::Acc (&acc)[Mma<IN>::NB][Mma<IN>::NB],
+                                          const int (&fb)[4], const typename M::Frags& Fm,
+                                          typename M::Frags& Fr, typename M::Acc (&acc)[M::NBM][M::NB],
                                           const X& extra) {
-  using M = Mma<IN>;
+  constexpr int kLoads = kOp == 0 ? M::kLoadsA : M::kLoadsB;
   const SlabLoad<kOp> L(c, smem, kt_issue, slot_issue);
 #pragma unroll
   for (int m = 0; m < M::kMfma; ++m) {
     M::mma(m, Fm, acc);
     if constexpr (kIssue) {
       const int d = (m - M::kDmaAt) / M::kDmaEvery;
-      if (m >= M::kDmaAt && (m - M::kDmaAt) % M::kDmaEvery == 0 && d < kLoadsPerOperand)
+      if (m >= M::kDmaAt && (m - M::kDmaAt) % M::kDmaEvery == 0 && d < kLoads)
         L.issue(c, d);
     }
     if constexpr (kRead) {
@@ -414,9 +510,10 @@ __device__ __forceinline__ void half_step(const TileCtx& c, uint8_t* smem, int k
   }
 }
 
-// Element-by-element epilogue of a wave's 128 x 128 block (any alignment).
+// Element-by-element epilogue of a wave's block (128 x 128, or 64 x 128 in a
+// half-height tile; any alignment).
 template <typename M, int OUT>
-__device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc (&acc)[M::NB][M::NB],
+__device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc (&acc)[M::NBM][M::NB],
                                                 const GemmParams& p, uint8_t* Dw, const uint8_t* Cw,
                                                 const uint8_t* Bw, int rows_left, int cols_left) {
   constexpr int OES = out_size<OUT>();
@@ -428,7 +525,7 @@ __device__ __forceinline__ void epilogue_direct(int lane, const typename M::Acc 
     bv[j] = (Bw && col < cols_left) ? load_out<OUT>(Bw, col) : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < M::NB; ++i) {
+  for (int i = 0; i < M::NBM; ++i) {
 #pragma unroll
     for (int r = 0; r < M::R; ++r) {
       const int row = M::out_row(i, r, lane);
@@ -607,7 +704,8 @@ __device__ __forceinline__ void epilogue_staged_c(uint8_t* smem, int wave, int l
   epilogue_c_part<M, 0>(base, lane, acc, p, Dw, Cf, ldc_b, has_bias, bb);
 }
 
-// bf16 output without C, whole 128 x 128 wave block, D rows 8-byte aligned:
+// bf16 output without C, whole wave block (128 x 128, or 64 x 128 in a
+// half-height tile), D rows 8-byte aligned:
 // the same fp32 staging as above, read back 4 consecutive values per lane,
 // rounded to bf16 (RNE, as the element-wise form) and stored as 8 bytes, so
 // a wave writes two 256-byte row pieces per store instead of 2 bytes per lane.
@@ -615,9 +713,10 @@ __device__ __forceinline__ void epilogue_staged_c(uint8_t* smem, int wave, int l
 // 16384 GEMM.  The caller has passed the workgroup barrier.
 template <typename M>
 __device__ __forceinline__ void epilogue_staged_bf16(uint8_t* smem, int wave, int lane,
-                                                     const typename M::Acc (&acc)[M::NB][M::NB],
+                                                     const typename M::Acc (&acc)[M::NBM][M::NB],
                                                      const GemmParams& p, uint8_t* Dw, const uint8_t* Bw) {
   constexpr int kBlocksPerQuarter = 32 / M::BLK;
+  constexpr int kQuarters = M::NBM / kBlocksPerQuarter;  // 32-row parts of the wave block
   float* const lds = reinterpret_cast<float*>(smem + wave * kEpiWaveStride);
   const int bc = 4 * (lane & 31);
   // the lane's four bias values (its columns are the same in every row)
@@ -627,7 +726,7 @@ __device__ __forceinline__ void epilogue_staged_bf16(uint8_t* smem, int wave, in
     for (int e = 0; e < 4; ++e) bv[e] = load_out<OUT_BF16>(Bw, bc + e);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kQuarters; ++q) {
 #pragma unroll
     for (int ib = 0; ib < kBlocksPerQuarter; ++ib) {
       const int i = q * kBlocksPerQuarter + ib;
@@ -771,12 +870,16 @@ struct NoAfterLoop {
 // One 256 x 256 tile (tm, tn) of batch l of the GEMM p, computed by the
 // whole workgroup with the LDS ring smem.  Every argument is workgroup-uniform.
 // kCopy: the tile also performs the copy *lc inside its K loop and calls
-// after_loop() (with every wave) once the loop is done.
-template <int IN, int OUT, bool kCopy = false, typename AfterLoop = NoAfterLoop>
+// after_loop() (with every wave) once the loop is done.  kHalf: only rows
+// 128 hrow .. 128 hrow + 127 of the tile (a half-height tile).
+template <int IN, int OUT, bool kCopy = false, bool kHalf = false, typename AfterLoop = NoAfterLoop>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, int tn, uint8_t* smem,
-                                          const LoopCopy* lc = nullptr, const AfterLoop& after_loop = {}) {
-  using M = Mma<IN>;
+                                          const LoopCopy* lc = nullptr, const AfterLoop& after_loop = {},
+                                          int hrow = 0) {
+  using M = std::conditional_t<kHalf, MmaHalf<IN>, Mma<IN>>;
   constexpr int ES = elem_size<IN>();
+  constexpr int kRows = kHalf ? kBM / 2 : kBM;  // rows of the tile
+  constexpr int kWaveRows = kRows / 2;          // rows of a wave's block
 
   // the lane index, redefined per tile: in the persistent kernel, nothing
   // derived from it is hoisted out of the tile loop (where it would hold
@@ -785,14 +888,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * kBM + (kHalf ? hrow * kRows : 0), n0 = tn * kBN;
 
   TileCtx c;
   c.Ab = static_cast<const uint8_t*>(p.A) + (l * p.sA + static_cast<int64_t>(m0) * p.lda) * ES;
   c.Bb = static_cast<const uint8_t*>(p.B) + (l * p.sB + static_cast<int64_t>(n0) * p.ldb) * ES;
   const uint32_t lda_b = static_cast<uint32_t>(p.lda * ES);
   const uint32_t ldb_b = static_cast<uint32_t>(p.ldb * ES);
-  c.a_bytes = static_cast<uint32_t>(min(kBM, p.M - m0)) * lda_b;
+  c.a_bytes = static_cast<uint32_t>(max(0, min(kRows, p.M - m0))) * lda_b;
   c.b_bytes = static_cast<uint32_t>(min(kBN, p.N - n0)) * ldb_b;
   c.kbytes = p.K * ES;
   c.lda16 = 16 * lda_b;
@@ -800,34 +903,37 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   const int KT = (c.kbytes + kSlab - 1) / kSlab;
 
   // DMA lane mapping.  Wave w fills blocks 8w .. 8w+7 of each operand
-  // slab; block b holds rows 8b .. 8b+7, so f(row) depends on b % 2 and
-  // on the lane's row within the block.
+  // slab (of an A slab of a half-height tile, blocks 4w .. 4w+3); block b
+  // holds rows 8b .. 8b+7, so f(row) depends on b % 2 and on the lane's row
+  // within the block, identically for A and B (the K chunk of a row's
+  // lanes does not depend on which of the two slabs the row is in).
   const int half = lane >> 5, brow = (lane >> 2) & 7, schunk = lane & 3;
 #pragma unroll
   for (int odd = 0; odd < 2; ++odd) {
-    const int row = 64 * wave + 8 * odd + brow;          // row of block 8w + odd
-    const int gch = half * 4 + (schunk ^ chunk_perm(row));
-    c.ga[odd] = row * lda_b + gch * 16;
-    c.gb[odd] = row * ldb_b + gch * 16;
+    const int r16 = 8 * odd + brow;  // the row mod 16 (the wave's first row is a multiple of 16)
+    const int gch = half * 4 + (schunk ^ chunk_perm(r16));
+    c.ga[odd] = (M::kLoadsA * 8 * wave + r16) * lda_b + gch * 16;  // A block kLoadsA w + odd
+    c.gb[odd] = (M::kLoadsB * 8 * wave + r16) * ldb_b + gch * 16;  // B block 8w + odd
     c.gk[odd] = gch * 16;
   }
-  c.fill = wave * 8 * 1024;
+  c.fillA = wave * M::kLoadsA * 1024;
+  c.fillB = wave * M::kLoadsB * 1024;
 
   // Fragment base offsets within an operand slab: [A even, A odd, B even,
   // B odd].  Rows of every read of a lane agree mod 16 with its base row.
   int fb[4];
 #pragma unroll
   for (int odd = 0; odd < 2; ++odd) {
-    const int ra = wm * 128 + M::base_row(lane, odd);
+    const int ra = wm * kWaveRows + M::base_row(lane, odd);
     const int rb = wn * 128 + M::base_row(lane, odd);
     const int q = M::base_chunk(lane, odd);
     fb[odd] = (ra >> 3) * 1024 + (ra & 7) * 64 + ((q ^ chunk_perm(ra)) << 4);
     fb[2 + odd] = (rb >> 3) * 1024 + (rb & 7) * 64 + ((q ^ chunk_perm(rb)) << 4);
   }
 
-  typename M::Acc acc[M::NB][M::NB];
+  typename M::Acc acc[M::NBM][M::NB];
 #pragma unroll
-  for (int i = 0; i < M::NB; ++i)
+  for (int i = 0; i < M::NBM; ++i)
 #pragma unroll
     for (int j = 0; j < M::NB; ++j) acc[i][j] = typename M::Acc{};
 
@@ -878,12 +984,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   };
 
   // Prologue: slabs 0 and 1 into slots 0..3; slab 0 landed; its half 0 read.
-  issue_operand<kLead>(c, smem, 0, 0);
-  issue_operand<kTrail>(c, smem, 0, 1);
+  constexpr int kLeadLoads = kLead == 0 ? M::kLoadsA : M::kLoadsB;
+  issue_operand<M, kLead>(c, smem, 0, 0);
+  issue_operand<M, kTrail>(c, smem, 0, 1);
   if (KT > 1) {
-    issue_operand<kLead>(c, smem, 1, 2);
-    issue_operand<kTrail>(c, smem, 1, 3);
-    wait_vmcnt<2 * kLoadsPerOperand>();
+    issue_operand<M, kLead>(c, smem, 1, 2);
+    issue_operand<M, kTrail>(c, smem, 1, 3);
+    wait_vmcnt<M::kLoadsA + M::kLoadsB>();
   } else {
     wait_vmcnt<0>();
   }
@@ -903,30 +1010,30 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   int kt = 0, s = 0;
   for (; kt + 2 < KT; ++kt) {
     wait_lgkmcnt0();
-    half_step<IN, true, true, kLead>(c, smem, kt + 2, slot_add(s, 4), abase(s) + 512, bbase(s) + 512, fb, F0, F1,
+    half_step<M, true, true, kLead>(c, smem, kt + 2, slot_add(s, 4), abase(s) + 512, bbase(s) + 512, fb, F0, F1,
                                      acc, none);
     wait_lgkmcnt0();
-    wait_vmcnt<kLoadsPerOperand>();
+    wait_vmcnt<kLeadLoads>();
     barrier_only();
-    half_step<IN, true, true, kTrail>(c, smem, kt + 2, s, abase(slot_add(s, 2)), bbase(slot_add(s, 2)), fb, F1,
+    half_step<M, true, true, kTrail>(c, smem, kt + 2, s, abase(slot_add(s, 2)), bbase(slot_add(s, 2)), fb, F1,
                                       F0, acc, [&](int m) { copy_ops(m, kt, true); });
     s = slot_add(s, 2);
   }
   if (kt + 1 < KT) {  // second to last slab: nothing left to prefetch
     wait_lgkmcnt0();
-    half_step<IN, false, true, kLead>(c, smem, kt, s, abase(s) + 512, bbase(s) + 512, fb, F0, F1, acc, none);
+    half_step<M, false, true, kLead>(c, smem, kt, s, abase(s) + 512, bbase(s) + 512, fb, F0, F1, acc, none);
     wait_lgkmcnt0();
     wait_vmcnt<0>();
     barrier_only();
-    half_step<IN, false, true, kTrail>(c, smem, kt, s, abase(slot_add(s, 2)), bbase(slot_add(s, 2)), fb, F1, F0,
+    half_step<M, false, true, kTrail>(c, smem, kt, s, abase(slot_add(s, 2)), bbase(slot_add(s, 2)), fb, F1, F0,
                                        acc, [&](int m) { copy_ops(m, kt, false); });
     s = slot_add(s, 2);
     ++kt;
   }
   wait_lgkmcnt0();  // last slab
-  half_step<IN, false, true, kLead>(c, smem, kt, s, abase(s) + 512, bbase(s) + 512, fb, F0, F1, acc, none);
+  half_step<M, false, true, kLead>(c, smem, kt, s, abase(s) + 512, bbase(s) + 512, fb, F0, F1, acc, none);
   wait_lgkmcnt0();
-  half_step<IN, false, false, kTrail>(c, smem, kt, s, smem, smem, fb, F1, F0, acc, none);
+  half_step<M, false, false, kTrail>(c, smem, kt, s, smem, smem, fb, F1, F0, acc, none);
   if constexpr (kCopy) after_loop();
   // The MFMAs are opaque to the compiler's hazard tracking: give the last
   // ones their result latency, then redefine every accumulator after that
@@ -935,7 +1042,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   // and returns the value without that half slab).
   asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < M::NB; ++i)
+  for (int i = 0; i < M::NBM; ++i)
 #pragma unroll
     for (int j = 0; j < M::NB; ++j) asm volatile("" : "+a"(acc[i][j]));
 
@@ -950,7 +1057,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   [[maybe_unused]] const uint64_t align = reinterpret_cast<uint64_t>(Dl) | static_cast<uint64_t>(p.ldd * OES) |
                          (use_c ? reinterpret_cast<uint64_t>(Cl) | static_cast<uint64_t>(p.ldc * OES) : 0) |
                          reinterpret_cast<uint64_t>(p.bias);
-  const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
+  const int wrow0 = m0 + wm * kWaveRows, wcol0 = n0 + wn * 128;
   const int rows_left = p.M - wrow0, cols_left = p.N - wcol0;
   uint8_t* Dw = const_cast<uint8_t*>(Dl) + (static_cast<int64_t>(wrow0) * p.ldd + wcol0) * OES;
   const uint8_t* Cw = use_c ? Cl + (static_cast<int64_t>(wrow0) * p.ldc + wcol0) * OES : nullptr;
@@ -964,14 +1071,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   if constexpr (OUT == OUT_E4M3) {
     // e4m3 output: element by element (one byte per value)
   } else if constexpr (OUT == OUT_F32) {
-    if ((align & 15) == 0) {
-      epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
-      return;
+    // (a half-height tile: element by element; no workload here ends in one)
+    if constexpr (!kHalf) {
+      if ((align & 15) == 0) {
+        epilogue_staged<M>(smem, wave, elane, acc, p, Dw, Cw, Bw, rows_left, cols_left);
+        return;
+      }
     }
   } else {
     if ((align & 7) == 0 && !use_c) {
       barrier_only();  // every wave is done with the operand ring (uniform branch)
-      if (rows_left >= 128 && cols_left >= 128) {
+      if (rows_left >= kWaveRows && cols_left >= 128) {
         epilogue_staged_bf16<M>(smem, wave, elane, acc, p, Dw, Bw);
         return;
       }
@@ -987,16 +1097,48 @@ gemm_tn_kernel(GemmParams p) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = (p.N + kBN - 1) / kBN;
   int tm, tn;
+  if (p.tail_cus > 0) {
+    // XCD x runs workgroups x, x + 8, .. in order: its item i is tile i of
+    // its range, except that the last partial round's tiles come as two
+    // half-height items each
+    const int T = tiles_m * tiles_n;
+    const int x = blockIdx.x % kNumXcd, i = blockIdx.x / kNumXcd;
+    const int q = T / kNumXcd, r = T % kNumXcd;
+    const int n = q + (x < r ? 1 : 0);
+    const int split = half_tail_tiles(n, p.tail_cus), whole = n - split;
+    if (i >= whole + 2 * split) return;  // padding of the grid (uniform)
+    if (i >= whole) {
+      order_tile(x * q + min(x, r) + whole + (i - whole) / 2, tiles_m, tiles_n, tm, tn);
+      gemm_tile<IN, OUT, false, true>(p, 0, tm, tn, smem, nullptr, NoAfterLoop{}, (i - whole) & 1);
+      return;
+    }
+    order_tile(x * q + min(x, r) + i, tiles_m, tiles_n, tm, tn);
+    gemm_tile<IN, OUT>(p, 0, tm, tn, smem);
+    return;
+  }
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   gemm_tile<IN, OUT>(p, blockIdx.y, tm, tn, smem);
 }
 
 template <int IN, int OUT>
-inline hipError_t launch_t(const GemmParams& p, hipStream_t stream) {
+inline hipError_t launch_t(GemmParams p, hipStream_t stream) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = (p.N + kBN - 1) / kBN;
-  const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
-                  static_cast<unsigned>(p.L));
+  const int T = tiles_m * tiles_n;
+  if (p.L != 1) p.tail_cus = 0;
+  unsigned gx = static_cast<unsigned>(T);
+  if (p.tail_cus > 0) {
+    // items of the XCD with the most: the first XCD's
+    const int n = T / kNumXcd + (T % kNumXcd ? 1 : 0);
+    const int split = half_tail_tiles(n, p.tail_cus);
+    const int n_other = T / kNumXcd;
+    const int most = std::max(n + split, n_other + half_tail_tiles(n_other, p.tail_cus));
+    if (split == 0 && half_tail_tiles(n_other, p.tail_cus) == 0)
+      p.tail_cus = 0;  // nothing to split: the plain mapping
+    else
+      gx = static_cast<unsigned>(most) * kNumXcd;
+  }
+  const dim3 grid(gx, static_cast<unsigned>(p.L));
   hipLaunchKernelGGL((gemm_tn_kernel<IN, OUT>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -315,6 +315,12 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     accumulate in reduced precision unless asked not to; gfx950's
  *     f8f6f4 MFMA accumulates in fp32 at full rate, so both settings run the
  *     same kernel and give the same bits.
+ *   DIST_GEMM_OPT_HALF_TILES: 1 (default) or 0.  When the last round of
+ *     an XCD's (mode 1: a work queue's) tiles would fill at most half of
+ *     its CUs, each of those tiles runs as two 128 x 256 half-height tiles
+ *     on two CUs, so the round takes about half as long.  Every element of
+ *     D is computed by the same instructions in the same order either way,
+ *     so the result is the same bit for bit.
  *   DIST_GEMM_OPT_COPY_DELAY_US: a test hook that holds back every shard
  *     copy by this many microseconds, in [0, 10^6] (default 0): in mode 1
  *     each workgroup starts its first copy piece no earlier than this long
@@ -338,7 +344,8 @@ enum dist_gemm_option {
   DIST_GEMM_OPT_COPY_AHEAD = 9,
   DIST_GEMM_OPT_SHARED_A = 10,
   DIST_GEMM_OPT_COPY_DELAY_US = 11,
-  DIST_GEMM_OPT_FAST_ACCUM = 12
+  DIST_GEMM_OPT_FAST_ACCUM = 12,
+  DIST_GEMM_OPT_HALF_TILES = 13
 };
 int dist_gemm_set_option(dist_gemm_plan_t plan, int option, int64_t value);
 

@@ -57,8 +57,15 @@ def lists(tb, copy_local):
     return [[0, n0 + nz], [n0 + nz, n0 + nz]]
 
 
-def simulate(tb, L, nq, n_wg, copy_local=False):
-    """Run the protocol; return (tiles seen, per-strip counters, claims)."""
+def half_tail_tiles(n, slots):
+    """Tiles of a last partial round that run as two half-height items."""
+    rem = n % slots
+    return rem if 0 < rem and 2 * rem <= slots else 0
+
+
+def simulate(tb, L, nq, n_wg, copy_local=False, half_tail=True):
+    """Run the protocol; return (tiles seen as (l, strip, other, half or -1),
+    per-strip counters, claims, end time)."""
     S = len(tb["steps"])
     LG = tb["LG"]
     ranges = lists(tb, copy_local)
@@ -96,12 +103,16 @@ def simulate(tb, L, nq, n_wg, copy_local=False):
     def workgroup(b):
         q = b % nq
         seg = tb["seg"][q]
-        n_items = seg[-1]
+        n_tiles = seg[-1]
+        split = half_tail_tiles(n_tiles, n_wg // nq) if half_tail else 0
+        whole, n_items = n_tiles - split, n_tiles + split
         while True:
-            k = qctr[q]
+            item = qctr[q]
             qctr[q] += 1
-            if k >= n_items:
+            if item >= n_items:
                 break
+            k = item if item < whole else whole + (item - whole) // 2
+            hrow = -1 if item < whole else (item - whole) % 2
             g = max(i for i in range(len(seg) - 1) if seg[i] <= k)
             nst = tb["segs"][g][1]
             T2 = tb["segs"][g][2]
@@ -138,8 +149,8 @@ def simulate(tb, L, nq, n_wg, copy_local=False):
                         yield ("block", None)
                 assert ctr.get(key, 0) >= own[3]
             mine = take(1, 1) if tb["loop"] else []
-            done_tiles.append((l, strip, ob))
-            yield ("delay", 100)
+            done_tiles.append((l, strip, ob, hrow))
+            yield ("delay", 100 if hrow < 0 else 50)
             for p in mine:
                 complete(p)
         for li in (0, 1):
@@ -243,20 +254,27 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("half_tail", [True, False])
 @pytest.mark.parametrize("copy_local", [False, True])
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[5]}_{c[0]}x{c[1]}x{c[2]}_L{c[3]}_tp{c[4]}_q{c[8]}g{c[9]}a{c[10]}w{c[12]}"
                                             for c in CASES])
-def test_tables_and_protocol(case, copy_local):
+def test_tables_and_protocol(case, copy_local, half_tail):
     M, N, K, L, TP, sched, dtype, shared_a, nq, group, ahead, chunk, n_wg = case
     if copy_local and not sched.startswith("AG"):
         pytest.skip("the gathered image is returned for the all-gather schedules only")
     tb = dg.dist_gemm_fused_tables(M, N, K, L, TP, sched, dtype, shared_a, nq, group, ahead, chunk, n_wg)
     check_tables(tb, M, N, L, TP, nq, n_wg, ahead)
-    tiles, ctr, claimed, t_end = simulate(tb, L, nq, n_wg, copy_local)
-    # every tile of the grid once
+    tiles, ctr, claimed, t_end = simulate(tb, L, nq, n_wg, copy_local, half_tail)
+    # every tile of the grid once, whole or as its two halves
     n_other = ((N if not tb["cols"] else M) + 255) // 256
     expect = sorted((l, s, o) for l in range(L) for s in range(tb["n_strips"]) for o in range(n_other))
-    assert sorted(tiles) == expect
+    whole = [t[:3] for t in tiles if t[3] < 0]
+    halves = sorted(t for t in tiles if t[3] >= 0)
+    assert halves[0::2] == sorted(t[:3] + (0,) for t in halves[1::2]) or not halves
+    assert [t[3] for t in halves] == [0, 1] * (len(halves) // 2)
+    assert sorted(whole + [t[:3] for t in halves[0::2]]) == expect
+    if not half_tail:
+        assert not halves
     # every piece claimed once; every staged strip (step 0's too with a returned image) complete
     total = tb["n_list0"] + tb["n_list1"] + (tb["n_local"] if copy_local else 0)
     assert sorted(claimed) == list(range(total))
