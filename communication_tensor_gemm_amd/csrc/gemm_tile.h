@@ -435,7 +435,7 @@ struct TileCtx {
   uint32_t ga[2], gb[2];      // per-lane global offsets for even / odd blocks
   uint32_t lda16, ldb16;      // 16 rows of A / B in bytes (block pair stride)
   uint32_t gk[2];             // lane's K byte offset within a slab, even / odd blocks
-  int kbytes;
+  int kshift;                 // bytes slab 0 starts before K = 0 (see SlabLoad)
   int fillA, fillB;           // wave's first LDS block within an A / B slab (bytes)
 };
 
@@ -444,36 +444,49 @@ __device__ __forceinline__ int slot_add(int s, int d) {
   return s >= kSlots ? s - kSlots : s;
 }
 
-// DMA state of one operand slab (OP 0: A, 1: B) of slab kt bound for a ring slot.
-template <int OP>
+// DMA state of one operand slab (OP 0: A, 1: B) of slab kt bound for a ring
+// slot.  Slab kt covers K bytes kt * 128 - kshift .. + 127: when K is not a
+// multiple of the slab, slab 0 is the partial one and starts before K = 0,
+// so every later slab lies wholly inside K and its loads need no per-lane
+// mask (an OR per load measured 1-3% of the bf16 main loop).  kMask (slab
+// 0 only): chunks before K = 0 get the top offset bit, so the load is out of
+// range and fills zeros.
+template <int OP, bool kMask = false>
 struct SlabLoad {
   __amdgpu_buffer_rsrc_t r;
   uint32_t kinv[2];
   uint8_t* dst;
   __device__ __forceinline__ SlabLoad(const TileCtx& c, uint8_t* smem, int kt, int slot) {
-    const uint32_t k0b = static_cast<uint32_t>(kt) * kSlab;
-    // chunks past K: top offset bit set, so the load is out of range (zeros)
-#pragma unroll
-    for (int odd = 0; odd < 2; ++odd)
-      kinv[odd] = (static_cast<int>(k0b + c.gk[odd]) < c.kbytes) ? 0u : kOutOfRange;
-    // bytes left from k0b (none: a half-height tile whose rows all lie past
-    // M has a_bytes = 0, and every load must then be out of range)
+    const uint8_t* const base = OP == 0 ? c.Ab : c.Bb;
     const uint32_t have = OP == 0 ? c.a_bytes : c.b_bytes;
-    r = make_rsrc((OP == 0 ? c.Ab : c.Bb) + k0b, have > k0b ? have - k0b : 0u);
+    if constexpr (kMask) {
+      // slab 0 (kt = 0): from -kshift
+#pragma unroll
+      for (int odd = 0; odd < 2; ++odd)
+        kinv[odd] = (c.gk[odd] >= static_cast<uint32_t>(c.kshift)) ? 0u : kOutOfRange;
+      r = make_rsrc(base - c.kshift, have + static_cast<uint32_t>(c.kshift));
+    } else {
+      // slab kt >= 1: from k0b > 0; bytes left from there (none: a
+      // half-height tile whose rows all lie past M has a_bytes = 0, and
+      // every load must then be out of range)
+      const uint32_t k0b = static_cast<uint32_t>(kt) * kSlab - static_cast<uint32_t>(c.kshift);
+      r = make_rsrc(base + k0b, have > k0b ? have - k0b : 0u);
+    }
     dst = smem + slot * kOperandSlab + (OP == 0 ? c.fillA : c.fillB);
   }
   // load d of the wave's: LDS block fill/1K + d, rows 8d.. of the wave's rows
   __device__ __forceinline__ void issue(const TileCtx& c, int d) const {
     const uint32_t* g = OP == 0 ? c.ga : c.gb;
     const uint32_t ld16 = OP == 0 ? c.lda16 : c.ldb16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024 * d), 16,
-                                             (g[d & 1] + (d >> 1) * ld16) | kinv[d & 1], 0, 0, 0);
+    uint32_t off = g[d & 1] + (d >> 1) * ld16;
+    if constexpr (kMask) off |= kinv[d & 1];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024 * d), 16, off, 0, 0, 0);
   }
 };
 
-template <typename M, int OP>
+template <typename M, int OP, bool kMask = false>
 __device__ __forceinline__ void issue_operand(const TileCtx& c, uint8_t* smem, int kt, int slot) {
-  const SlabLoad<OP> L(c, smem, kt, slot);
+  const SlabLoad<OP, kMask> L(c, smem, kt, slot);
 #pragma unroll
   for (int d = 0; d < (OP == 0 ? M::kLoadsA : M::kLoadsB); ++d) L.issue(c, d);
 }
@@ -897,10 +910,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   const uint32_t ldb_b = static_cast<uint32_t>(p.ldb * ES);
   c.a_bytes = static_cast<uint32_t>(max(0, min(kRows, p.M - m0))) * lda_b;
   c.b_bytes = static_cast<uint32_t>(min(kBN, p.N - n0)) * ldb_b;
-  c.kbytes = p.K * ES;
+  const int kbytes = p.K * ES;
   c.lda16 = 16 * lda_b;
   c.ldb16 = 16 * ldb_b;
-  const int KT = (c.kbytes + kSlab - 1) / kSlab;
+  const int KT = (kbytes + kSlab - 1) / kSlab;
+  c.kshift = KT * kSlab - kbytes;
 
   // DMA lane mapping.  Wave w fills blocks 8w .. 8w+7 of each operand
   // slab (of an A slab of a half-height tile, blocks 4w .. 4w+3); block b
@@ -985,8 +999,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
 
   // Prologue: slabs 0 and 1 into slots 0..3; slab 0 landed; its half 0 read.
   constexpr int kLeadLoads = kLead == 0 ? M::kLoadsA : M::kLoadsB;
-  issue_operand<M, kLead>(c, smem, 0, 0);
-  issue_operand<M, kTrail>(c, smem, 0, 1);
+  issue_operand<M, kLead, true>(c, smem, 0, 0);
+  issue_operand<M, kTrail, true>(c, smem, 0, 1);
   if (KT > 1) {
     issue_operand<M, kLead>(c, smem, 1, 2);
     issue_operand<M, kTrail>(c, smem, 1, 3);
