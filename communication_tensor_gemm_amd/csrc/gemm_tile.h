@@ -436,6 +436,7 @@ struct TileCtx {
   uint32_t lda16, ldb16;      // 16 rows of A / B in bytes (block pair stride)
   uint32_t gk[2];             // lane's K byte offset within a slab, even / odd blocks
   int kshift;                 // bytes slab 0 starts before K = 0 (see SlabLoad)
+  __amdgpu_buffer_rsrc_t rA, rB;  // the tile's valid rows of A / B from K = 0
   int fillA, fillB;           // wave's first LDS block within an A / B slab (bytes)
 };
 
@@ -451,26 +452,32 @@ __device__ __forceinline__ int slot_add(int s, int d) {
 // mask (an OR per load measured 1-3% of the bf16 main loop).  kMask (slab
 // 0 only): chunks before K = 0 get the top offset bit, so the load is out of
 // range and fills zeros.
+//
+// Slabs kt >= 1 use the tile's descriptor (its valid rows from K = 0) with
+// the slab's K offset as the scalar offset, so a slab costs no descriptor
+// arithmetic: a lane of a valid row reads below the row's end (the slab lies
+// inside K, and K <= the leading dimension), a lane of a row past the valid
+// ones is out of range by its vector offset alone, with or without the
+// scalar offset in the range check.  (A half-height tile whose rows all lie
+// past M has no valid rows: every load is out of range.)
 template <int OP, bool kMask = false>
 struct SlabLoad {
   __amdgpu_buffer_rsrc_t r;
   uint32_t kinv[2];
+  uint32_t soff;
   uint8_t* dst;
   __device__ __forceinline__ SlabLoad(const TileCtx& c, uint8_t* smem, int kt, int slot) {
-    const uint8_t* const base = OP == 0 ? c.Ab : c.Bb;
-    const uint32_t have = OP == 0 ? c.a_bytes : c.b_bytes;
     if constexpr (kMask) {
       // slab 0 (kt = 0): from -kshift
 #pragma unroll
       for (int odd = 0; odd < 2; ++odd)
         kinv[odd] = (c.gk[odd] >= static_cast<uint32_t>(c.kshift)) ? 0u : kOutOfRange;
-      r = make_rsrc(base - c.kshift, have + static_cast<uint32_t>(c.kshift));
+      r = make_rsrc((OP == 0 ? c.Ab : c.Bb) - c.kshift,
+                    (OP == 0 ? c.a_bytes : c.b_bytes) + static_cast<uint32_t>(c.kshift));
+      soff = 0;
     } else {
-      // slab kt >= 1: from k0b > 0; bytes left from there (none: a
-      // half-height tile whose rows all lie past M has a_bytes = 0, and
-      // every load must then be out of range)
-      const uint32_t k0b = static_cast<uint32_t>(kt) * kSlab - static_cast<uint32_t>(c.kshift);
-      r = make_rsrc(base + k0b, have > k0b ? have - k0b : 0u);
+      r = OP == 0 ? c.rA : c.rB;
+      soff = static_cast<uint32_t>(kt) * kSlab - static_cast<uint32_t>(c.kshift);
     }
     dst = smem + slot * kOperandSlab + (OP == 0 ? c.fillA : c.fillB);
   }
@@ -480,7 +487,7 @@ struct SlabLoad {
     const uint32_t ld16 = OP == 0 ? c.lda16 : c.ldb16;
     uint32_t off = g[d & 1] + (d >> 1) * ld16;
     if constexpr (kMask) off |= kinv[d & 1];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024 * d), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 1024 * d), 16, off, soff, 0, 0);
   }
 };
 
@@ -915,6 +922,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   c.ldb16 = 16 * ldb_b;
   const int KT = (kbytes + kSlab - 1) / kSlab;
   c.kshift = KT * kSlab - kbytes;
+  c.rA = make_rsrc(c.Ab, c.a_bytes);
+  c.rB = make_rsrc(c.Bb, c.b_bytes);
 
   // DMA lane mapping.  Wave w fills blocks 8w .. 8w+7 of each operand
   // slab (of an A slab of a half-height tile, blocks 4w .. 4w+3); block b
