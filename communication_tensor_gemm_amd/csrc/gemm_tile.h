@@ -969,7 +969,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int l, int tm, in
   u32x4 cb[kLoopCopyOps];
   const uint32_t cvoff = static_cast<uint32_t>(wave) * (kLoopCopyOps * 1024) + static_cast<uint32_t>(lane) * 16;
   const int n_chunks = kCopy ? __builtin_amdgcn_readfirstlane(lc->chunks) : 0;
-  const int stride = n_chunks > 0 ? max(1, (KT - 2) / n_chunks) : 1;
+  const int stride = n_chunks > 0 ? max(1, (KT - 2) / max(n_chunks, 1)) : 1;
   const __amdgpu_buffer_rsrc_t csrc = make_rsrc(kCopy ? lc->src : nullptr, kCopy ? lc->bytes : 0);
   const __amdgpu_buffer_rsrc_t cdst = make_rsrc(kCopy ? lc->dst : nullptr, kCopy ? lc->bytes : 0);
   int ld_j = 0, ld_at = 0;  // the next chunk to load and its slab
