@@ -499,7 +499,7 @@ def main():
                     help="0 = step launches + side-stream copies, 1 = one persistent launch per run")
     ap.add_argument("--queues", type=int, default=8, help="work queues of the single launch (1 or 8)")
     ap.add_argument("--copy-chunk", type=int, default=2 << 20, help="bytes per copy item of the single launch")
-    ap.add_argument("--copy-ahead", type=int, default=1,
+    ap.add_argument("--copy-ahead", type=int, default=0,
                     help="segments of the single launch whose tiles claim a copy quota before their GEMM")
     ap.add_argument("--half-tiles", type=int, default=1,
                     help="1: a last round of tiles that fills at most half the CUs runs as half-height tiles")

@@ -126,7 +126,7 @@ def dist_gemm_step_table(M, N, K, L, TP, schedule, dtype) -> List[tuple]:
     return [s.as_tuple() for s in arr]
 
 
-def dist_gemm_fused_tables(M, N, K, L, TP, schedule, dtype, shared_a=0, queues=8, step_group=2, copy_ahead=1,
+def dist_gemm_fused_tables(M, N, K, L, TP, schedule, dtype, shared_a=0, queues=8, step_group=2, copy_ahead=0,
                            copy_chunk=2 << 20, n_wg=256) -> dict:
     """The single launch's tables for these options (host only): the info
     fields, and the arrays segs [n_segs][4], steps [TP][7], strips

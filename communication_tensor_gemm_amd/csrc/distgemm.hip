@@ -226,7 +226,7 @@ struct dist_gemm_plan_s {
   int n_segs = 0;             // segments in the device tables
   int n_list0 = 0, n_list1 = 0, n_local = 0;  // copy pieces: of claim lists 0 and 1; of step 0
   bool fused_loop = false;                    // list-1 pieces are copied inside K loops
-  int copy_ahead = 1;         // segments whose tiles claim a copy quota before their GEMM
+  int copy_ahead = 0;         // segments whose tiles claim a copy quota before their GEMM
   bool captured = false;      // a run was captured into a graph: tables are fixed
   std::vector<char> t_fused;  // [run % step_timing]: the run was one launch
   float scale_a = 1.0f, scale_b = 1.0f;
@@ -569,7 +569,7 @@ struct FusedTables {
 struct FusedOpts {
   int queues = dg::kMaxQueues;
   int64_t copy_chunk = 2 << 20;
-  int copy_ahead = 1;
+  int copy_ahead = 0;
   int max_group = 2;
   int n_wg = 256;  // workgroups of the launch
 };

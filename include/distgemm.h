@@ -285,13 +285,14 @@ int dist_gemm_set_bias(dist_gemm_plan_t plan, const void* bias);
  *     time.  Waits run out when the launch cannot keep a workgroup running
  *     on every work queue (other kernels holding the device's CUs), never
  *     in an unshared device; 0 makes every wait copy its own strip.
- *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 0..64; default 1.  The staged
+ *   DIST_GEMM_OPT_COPY_AHEAD (mode 1): D in 0..64; default 0.  The staged
  *     shards are copied in pieces from two lists: list 0, the steps the
  *     launch's first round of tiles reads, and list 1, the later steps.
- *     Every tile of the first D segments (default: the local step's, which
+ *     Every tile of the first D segments (D = 1: the local step's, which
  *     wait for nothing) claims a quota of list 0 before its GEMM (list 0 /
  *     (those tiles + the staged tiles of the first round)); a tile whose
- *     strip is not complete copies pieces while it waits.  For row strips
+ *     strip is not complete copies pieces while it waits (with D = 0 those
+ *     tiles copy all of list 0, and the local step's start at once).  For row strips
  *     (AG_ROT_A, AG_ROT_B, RS_TILE_A_ROT_C) whose rows are a multiple of 16
  *     bytes, with K of at least 6 slabs (over 640 bytes of a row of A) and
  *     steps left after those the first round reads, list 1 is copied
