@@ -84,6 +84,23 @@ def test_last_round_split_matches_whole_tiles(sched, dtype, M, N, K, beta):
     assert torch.equal(on, off)
 
 
+@pytest.mark.parametrize("sched,dtype,beta", [
+    ("AG_ROT_A", "BF16_F32", 0.0),
+    ("RS_TILE_B_ROT_C", "E4M3_BF16", 1.0),
+])
+def test_batched_split_tiles(sched, dtype, beta):
+    # L = 3 batches of 600 x 520: the single launch's queues hold 27 tiles of
+    # three batches, every one split; the monolithic GEMM splits only L = 1
+    import torch
+    w = workloads.small_case(f"half_batched_{sched}_{dtype}", sched, dtype, 600, 520, 272, 3, 4, 1.0, beta,
+                             seed=43)
+    x = workloads.generate(w)
+    log("case", w.name)
+    on, off = _both(w, x)
+    assert torch.equal(on, off)
+    check_full(w, x, on)
+
+
 def test_half_tiles_option_values():
     import communication_tensor_gemm_amd as dg
     with dg.Plan(256, 256, 64, 1, 2, "AG_ROT_A", "BF16_F32") as p:
