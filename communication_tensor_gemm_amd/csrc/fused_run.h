@@ -30,25 +30,27 @@
 // contiguous range of each segment's tile order, walked in groups of four
 // strips; nq = 1: one queue for the chip), in queue order, by an atomic
 // counter: queue q lists its tiles of segment 0 (step 0), then of segment
-// 1 (the next steps), and so on.
+// 1 (the next steps), and so on; when the queue's last round of tiles
+// would fill at most half of its workgroups, those tiles come as two
+// half-height items each.
 //
 // Copies.  The staged strips are cut into pieces, numbered in step order
 // (steps 1 .. S-1, then the local step when the gathered image is
 // returned), and handed out by two atomic claim counters over consecutive
 // ranges of that order: list 0 holds the steps that tiles of the launch's
 // first round read, list 1 the later steps.  List 0 goes first, in small
-// pieces copied through LDS by every workgroup of the first round: the
-// tiles of the first segments (which read the local shard) claim a quota
-// before their GEMM, and a tile of a staged strip that is not yet complete
-// claims pieces one at a time while it waits (list 0, then, for a strip of
-// list 1, list 1) instead of spinning.  A tile that starts its GEMM claims
-// one piece of list 1 and copies it inside its K loop, where the copy's
-// loads and stores ride in the shadow of the MFMAs; list-1 pieces are sized
-// so that the tiles starting before a step's segment carry all of its
-// pieces.  (Where a piece cannot be copied inside the loop -- column
-// strips, unaligned rows, too few slabs -- list 1 is empty and list 0 holds
-// every staged step.)  Workgroups whose queue is empty claim whatever is
-// left.
+// pieces copied through LDS by the workgroups of the first round: a tile of
+// a staged strip that is not yet complete claims pieces one at a time while
+// it waits (list 0, then, for a strip of list 1, list 1) instead of
+// spinning, and the tiles of the first COPY_AHEAD segments (default none;
+// those read the local shard) first claim a quota before their GEMM.  A
+// tile that starts its GEMM claims one piece of list 1 and copies it inside
+// its K loop, where the copy's loads and stores ride in the shadow of the
+// MFMAs; list-1 pieces are sized so that the tiles starting before a
+// step's segment carry all of its pieces.  (Where a piece cannot be copied
+// inside the loop -- column strips, unaligned rows, too few slabs -- list 1
+// is empty and list 0 holds every staged step.)  Workgroups whose queue is
+// empty claim whatever is left.
 //
 // Progress.  A workgroup copies what it claims before it waits on
 // anything (an in-loop piece is claimed only once the tile's own wait is
