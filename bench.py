@@ -250,10 +250,19 @@ TRAFFIC_FILE = "profiles/fused_run_kernel_hbm_traffic.txt"
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments, blank lines and trailing
+    blanks removed, so that a comment edit leaves a recorded measurement
+    valid and any code change invalidates it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        text = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        # // comments (a "//" inside a string literal is not one: the sources have none)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [l.rstrip() for l in text.splitlines()]
+        h.update("\n".join(l for l in lines if l).encode())
     return h.hexdigest()[:16]
 
 
