@@ -14,6 +14,8 @@ Printed: one JSON line on stdout.  Progress goes to stderr.
                its mean duration, from HIP events recorded around every
                launch on the stream it runs on, over the timed region
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+  vendor_context  context only: torch's GEMM (hipBLASLt) on the monolithic
+               shape on the same device
 """
 from __future__ import annotations
 
@@ -368,6 +370,53 @@ def copy_alone_ms(w, A, B, C, reps=5):
             "what": "the S-1 staged shards copied by a plain device copy (torch copy_), GPU otherwise idle"}
 
 
+def vendor_context(w, mono_ms, reps=20):
+    """Context only, outside the product: the vendor library (hipBLASLt
+    through torch) on the monolithic shape, same device, random operands of
+    the input type.  bf16 and fp32: torch.matmul(A, B^T) (bf16 output for
+    bf16 inputs, no C); e4m3: torch._scaled_mm with unit scales, bf16 output.
+    Not a like-for-like comparison where the output type or the C read
+    differ; reported so that the GEMM kernel can be read against the
+    device's own library."""
+    import torch
+    out = {}
+    try:
+        M, N, K = w.M, w.N, w.K
+        g = torch.Generator(device="cuda")
+        g.manual_seed(0)
+        if w.in_dtype == "e4m3":
+            A = (torch.randn(M, K, device="cuda", generator=g) * 64).to(torch.float8_e4m3fn)
+            B = (torch.randn(N, K, device="cuda", generator=g) * 64).to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda")
+            fn = lambda: torch._scaled_mm(A, B.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)  # noqa: E731
+            what = "torch._scaled_mm, e4m3 in, bf16 out"
+        else:
+            dt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+            A = torch.randn(M, K, device="cuda", generator=g).to(dt)
+            B = torch.randn(N, K, device="cuda", generator=g).to(dt)
+            fn = lambda: torch.matmul(A, B.t())  # noqa: E731
+            what = f"torch.matmul, {w.in_dtype} in and out, no C"
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out = {"what": what, "ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+        if mono_ms:
+            out["our_monolithic_over_it"] = round(ms / mono_ms, 4)
+    except Exception as e:  # context only: never fails the bench
+        out = {"error": f"{type(e).__name__}: {str(e)[:200]}"}
+    finally:
+        A = B = None
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure(w, args, headline):
     """Time one workload: the schedule, its monolithic GEMM, parity, the
     rotation's copy alone; the sustained clock for the headline only."""
@@ -448,6 +497,10 @@ def measure(w, args, headline):
             f"schedule overhead {100 * mono['exposed_overhead']:.1f}%")
     copy_alone = copy_alone_ms(w, A, B, C) if S > 1 else None
     log(f"[bench] rotation copy alone: {copy_alone}")
+    vendor = None
+    if not args.no_vendor and w.L == 1:
+        vendor = vendor_context(w, mono["ms"] if mono else None)
+        log(f"[bench] vendor library on the monolithic shape (context): {vendor}")
     wait_timeouts = plan.device_errors()
     sclk_stats = None
     if headline:
@@ -486,6 +539,7 @@ def measure(w, args, headline):
         "flushed": flushed,
         "parity": parity,
         "device_wait_timeouts": wait_timeouts,
+        "vendor_context": vendor,
     }
     return rec, x, sclk_stats
 
@@ -516,6 +570,8 @@ def main():
                     help="oracle sample: rows per step block for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-mono", action="store_true", help="skip the monolithic comparison")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor-library context timing of the monolithic shape")
     ap.add_argument("--flush", action="store_true",
                     help="also time runs with a 1 GiB scratch write before each (cold caches), reported separately")
     ap.add_argument("--no-sub", action="store_true",
@@ -590,6 +646,7 @@ def main():
         "flushed": rec["flushed"],
         "parity": rec["parity"],
         "device_wait_timeouts": rec["device_wait_timeouts"],
+        "vendor_context": rec["vendor_context"],
         "cpu_baseline": cpu,
         # the other TP=8 shard shapes of the metric, measured the same way in
         # the same process (not part of value)
